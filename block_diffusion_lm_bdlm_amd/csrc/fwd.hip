@@ -1,0 +1,345 @@
+// fwd.hip — forward of BDLM attention over one call's key set.
+//
+// O_i = sum_j softmax_j(s_ij) v_j with s_ij = scale q_i . k_j over the keys j
+// the mask lets row i see ("CSBP 完全拆解", CP attention equation and the
+// key/value set [K_b; K^clean_<b] of a corrupted block), plus
+// LSE_i = ln sum_j exp(s_ij).  The softmax is taken online over key tiles
+// in fp32 (running max and normaliser), with scores in base 2.
+//
+// bf16 kernel: a workgroup of 4 waves owns a 128-row query tile (32 rows
+// per wave, the rows held as the B operand of S^T = K Q^T) and walks the
+// key tiles of 64 keys that any of its rows can see.  K tiles (natural) and
+// V^T tiles (fp16) are staged through LDS, double buffered.  A key tile that
+// no row sees is never visited; a tile every row sees fully skips the mask.
+#include "device.h"
+#include "kernels.h"
+#include "walk.h"
+
+namespace bd {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int D>
+struct FwdSmem {
+  static constexpr int KS = D + 8;    // K row stride (bf16 elements)
+  static constexpr int VS = kBK + 8;  // V^T row stride (fp16 elements)
+  uint16_t k[2][kBK * KS];
+  _Float16 v[2][D * VS];
+};
+
+template <int D>
+__device__ inline void fwd_load_tile(const FwdArgs& A, const Plan& P, int b, int g, int c, int tid,
+                                     u32x4 (&kr)[D / 32], u32x4 (&vr)[D / 32]) {
+  const uint16_t* kb = A.kn + ((int64_t)(b * P.hkv + g) * P.nkc + c) * D;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int ch = tid + 256 * j;  // chunk of 8 elements
+    const int key = ch / (D / 8), dc = ch % (D / 8);
+    kr[j] = ldg16(kb + key * D + dc * 8);
+  }
+  const _Float16* vb = A.vt + (int64_t)(b * P.hkv + g) * D * P.nkc + c;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int ch = tid + 256 * j;
+    const int d = ch / (kBK / 8), kc = ch % (kBK / 8);
+    vr[j] = ldg16(vb + (int64_t)d * P.nkc + kc * 8);
+  }
+}
+
+template <int D>
+__device__ inline void fwd_store_tile(FwdSmem<D>& sm, int buf, int tid, const u32x4 (&kr)[D / 32],
+                                      const u32x4 (&vr)[D / 32]) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int ch = tid + 256 * j;
+    const int key = ch / (D / 8), dc = ch % (D / 8);
+    *reinterpret_cast<u32x4*>(&sm.k[buf][key * FwdSmem<D>::KS + dc * 8]) = kr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const int ch = tid + 256 * j;
+    const int d = ch / (kBK / 8), kc = ch % (kBK / 8);
+    *reinterpret_cast<u32x4*>(&sm.v[buf][d * FwdSmem<D>::VS + kc * 8]) = vr[j];
+  }
+}
+
+template <int D>
+__device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b, int h, int g,
+                         int32_t tile) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const QSeg S = P.q[seg_of_tile(P, tile)];
+  const int32_t r0 = (tile - S.tile0) * kBQ;
+  const int32_t n = min(kBQ, S.nrows - r0);
+  const int32_t rq = wave * 32 + ql;
+  const int32_t rc = min(rq, n - 1);
+  const bool clean = S.kind == KIND_CLEAN;
+
+  // this lane's query row (B operand: Q[row][ks*16 + hh*8 .. +8])
+  const TensorArg& QT = clean ? A.q_clean : A.q_corr;
+  const uint16_t* qp = static_cast<const uint16_t*>(QT.p) + b * QT.bs +
+                       (int64_t)(S.src0 + r0 + rc) * QT.rs + (int64_t)h * QT.hs;
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = ld16<bf16x8>(qp + ks * 16 + hh * 8);
+
+  const RowBounds rb = row_bounds(P, S, r0 + rc);
+  KeyWalk w;
+  keywalk_build(P, S, r0, r0 + n - 1, w);
+
+  const float c2 = P.scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+
+  if (w.total > 0) {
+    u32x4 kr[D / 32], vr[D / 32];
+    {
+      int32_t c, ri;
+      keywalk_at(w, 0, &c, &ri);
+      fwd_load_tile<D>(A, P, b, g, c, tid, kr, vr);
+      fwd_store_tile<D>(sm, 0, tid, kr, vr);
+    }
+    __syncthreads();
+    for (int32_t t = 0; t < w.total; ++t) {
+      const int buf = t & 1;
+      int32_t c, ri;
+      keywalk_at(w, t, &c, &ri);
+      if (t + 1 < w.total) {
+        int32_t cn, rn;
+        keywalk_at(w, t + 1, &cn, &rn);
+        fwd_load_tile<D>(A, P, b, g, cn, tid, kr, vr);
+      }
+      // S^T = K Q^T for two blocks of 32 keys
+      f32x16 sacc[2];
+      const uint16_t* kbase = sm.k[buf];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 a = ld16<bf16x8>(kbase + (kb * 32 + ql) * FwdSmem<D>::KS + ks * 16 + hh * 8);
+          sacc[kb] = mfma_bf16(a, qreg[ks], sacc[kb]);
+        }
+      }
+      const bool full = keywalk_full(w, ri, c);
+      if (!full) {
+        int32_t vlo, vhi;
+        compact_range(P.k[ri], rb, clean, &vlo, &vhi);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int32_t key = c + kb * 32 + crow(i, hh);
+            if (key < vlo || key >= vhi) sacc[kb][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = wave_max32(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float mc = m_use * c2;
+      const float alpha = __builtin_amdgcn_exp2f(m_run * c2 - mc);
+      float lsum = 0.f;
+      f16x8 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -mc));
+          lsum += p;
+          pf[kb][i >> 3][i & 7] = (_Float16)p;
+        }
+      l_run = l_run * alpha + lsum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      }
+      m_run = m_new;
+      // O^T += V^T P^T
+      const _Float16* vbase = sm.v[buf];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss) {
+            const f16x8 a =
+                ld16<f16x8>(vbase + (db * 32 + ql) * FwdSmem<D>::VS + kb * 32 + ss * 16 + hh * 8);
+            oacc[db] = mfma_f16(a, pf[kb][ss], oacc[db]);
+          }
+      if (t + 1 < w.total) fwd_store_tile<D>(sm, buf ^ 1, tid, kr, vr);
+      __syncthreads();
+    }
+  }
+
+  // epilogue: O = acc / l, LSE = (m * c2 + log2 l) * ln 2
+  const float l = wave_sum32(l_run);
+  if (rq < n) {
+    const int32_t row = S.row0 + r0 + rq;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t obase = b * A.o_bs + (int64_t)row * A.o_rs + (int64_t)h * A.o_hs;
+    if (A.o_f32) {
+      float* op = static_cast<float*>(A.o) + obase;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          f32x4 v = {oacc[db][i] * inv, oacc[db][i + 1] * inv, oacc[db][i + 2] * inv,
+                     oacc[db][i + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + db * 32 + crow(i, hh)) = v;
+        }
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(A.o) + obase;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          const uint32_t lo = bf16_bits(oacc[db][i] * inv) | ((uint32_t)bf16_bits(oacc[db][i + 1] * inv) << 16);
+          const uint32_t hi = bf16_bits(oacc[db][i + 2] * inv) | ((uint32_t)bf16_bits(oacc[db][i + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(op + db * 32 + crow(i, hh)) = make_uint2(lo, hi);
+        }
+    }
+    if (hh == 0) {
+      const float m_fin = (m_run == -INFINITY) ? 0.f : m_run;
+      A.lse[((int64_t)b * P.R + row) * P.hq + h] =
+          l > 0.f ? (m_fin * c2 + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const Plan P, const FwdArgs A) {
+  __shared__ FwdSmem<D> sm;
+  const WgQ wg = decode_wg_q(P, blockIdx.x);
+  fwd_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);
+  if (wg.tile_b >= 0) fwd_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_b);
+}
+
+// ------------------------------------------------------------------ fp32
+// Exact-precision path for fp32 inputs: two lanes per query row (lane l and
+// l+32 each own half of d), scores from LDS-staged fp32 K tiles on the
+// vector ALUs, the same online softmax, V accumulated in fp32.
+template <int D>
+struct F32Smem {
+  float k[kBK][D + 1];
+  float v[kBK][D + 1];
+};
+
+template <int D>
+__device__ void fwd_f32_tile(const Plan& P, const FwdF32Args& A, F32Smem<D>& sm, int b, int h, int g,
+                             int32_t tile) {
+  constexpr int DH = D / 2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const QSeg S = P.q[seg_of_tile(P, tile)];
+  const int32_t r0 = (tile - S.tile0) * kBQ;
+  const int32_t n = min(kBQ, S.nrows - r0);
+  const int32_t rq = wave * 32 + ql;
+  const int32_t rc = min(rq, n - 1);
+  const bool clean = S.kind == KIND_CLEAN;
+  const TensorArg& QT = clean ? A.q_clean : A.q_corr;
+  const float* qp = static_cast<const float*>(QT.p) + b * QT.bs + (int64_t)(S.src0 + r0 + rc) * QT.rs +
+                    (int64_t)h * QT.hs + hh * DH;
+  float q[DH], o[DH];
+#pragma unroll
+  for (int t = 0; t < DH; ++t) {
+    q[t] = qp[t];
+    o[t] = 0.f;
+  }
+  const RowBounds rb = row_bounds(P, S, r0 + rc);
+  KeyWalk w;
+  keywalk_build(P, S, r0, r0 + n - 1, w);
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int32_t t = 0; t < w.total; ++t) {
+    int32_t c, ri;
+    keywalk_at(w, t, &c, &ri);
+    const KSeg K = P.k[ri];
+    const TensorArg& KT = K.kind == KIND_CLEAN ? A.k_clean : A.k_corr;
+    const TensorArg& VT = K.kind == KIND_CLEAN ? A.v_clean : A.v_corr;
+    __syncthreads();
+    for (int e = tid; e < kBK * D; e += 256) {
+      const int key = e / D, dd = e % D;
+      const int32_t cc = c + key;
+      float kv = 0.f, vv = 0.f;
+      if (cc < K.c0 + K.len) {
+        const int64_t row = K.t0 + (cc - K.c0);
+        kv = static_cast<const float*>(KT.p)[b * KT.bs + row * KT.rs + (int64_t)g * KT.hs + dd];
+        vv = static_cast<const float*>(VT.p)[b * VT.bs + row * VT.rs + (int64_t)g * VT.hs + dd];
+      }
+      sm.k[key][dd] = kv;
+      sm.v[key][dd] = vv;
+    }
+    __syncthreads();
+    int32_t vlo, vhi;
+    compact_range(K, rb, clean, &vlo, &vhi);
+    float s[kBK];
+    float mx = -INFINITY;
+    for (int key = 0; key < kBK; ++key) {
+      float acc = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < DH; ++t2) acc = fmaf(q[t2], sm.k[key][hh * DH + t2], acc);
+      acc += __shfl_xor(acc, 32, 64);
+      const int32_t cc = c + key;
+      s[key] = (cc >= vlo && cc < vhi) ? acc * P.scale : -INFINITY;
+      mx = fmaxf(mx, s[key]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = expf(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int t2 = 0; t2 < DH; ++t2) o[t2] *= alpha;
+    for (int key = 0; key < kBK; ++key) {
+      const float p = expf(s[key] - m_use);
+      l_run += p;
+#pragma unroll
+      for (int t2 = 0; t2 < DH; ++t2) o[t2] = fmaf(p, sm.v[key][hh * DH + t2], o[t2]);
+    }
+    m_run = m_new;
+  }
+  if (rq < n) {
+    const int32_t row = S.row0 + r0 + rq;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* op = A.o + b * A.o_bs + (int64_t)row * A.o_rs + (int64_t)h * A.o_hs + hh * DH;
+#pragma unroll
+    for (int t2 = 0; t2 < DH; ++t2) op[t2] = o[t2] * inv;
+    if (hh == 0)
+      A.lse[((int64_t)b * P.R + row) * P.hq + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const Plan P, const FwdF32Args A) {
+  __shared__ F32Smem<D> sm;
+  const WgQ wg = decode_wg_q(P, blockIdx.x);
+  fwd_f32_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);
+  if (wg.tile_b >= 0) fwd_f32_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_b);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s) {
+  if (P.nwg_q == 0) return hipSuccess;
+  if (P.d == 128)
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
+  else
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const Plan& P, const FwdF32Args& a, hipStream_t s) {
+  if (P.nwg_q == 0) return hipSuccess;
+  if (P.d == 128)
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
+  else
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
+  return hipGetLastError();
+}
+
+}  // namespace bd
