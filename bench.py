@@ -1,0 +1,194 @@
+"""Benchmark: BDLM attention forward + backward on one MI355X.
+
+Default workload (the headline metric's configuration): whole BDLM mask at
+L = 65536 clean tokens (131072 positions), block size M = 32, batch 1,
+40 query heads / 8 KV heads, d_h = 128, bf16 inputs ~ N(0, 1), synthetic.
+One step = zero the gradient accumulators, forward (bf16 O, fp32 LSE),
+backward (dQ, dK, dV) — the whole hot path, nothing skipped.
+
+Useful FLOPs count visible (query, key) pairs only: 4 d per pair forward and
+10 d per pair backward, pairs per head = L (L + M) for the block-causal
+clean copy.  Printed as one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (batch, L, M, hq, hkv, d)
+    "bdlm_L64K_M32_h40kv8_d128": (1, 65536, 32, 40, 8, 128),
+    "bdlm_L8K_M32_b2_h16kv8_d128": (2, 8192, 32, 16, 8, 128),
+}
+DEFAULT = "bdlm_L64K_M32_h40kv8_d128"
+
+
+def visible_pairs(L, M):
+    return L * (L + M)
+
+
+def kernel_flops(name, pairs, hq, batch, d):
+    """Algorithmic FLOPs one launch of each kernel performs on visible pairs:
+    forward 4d (QK^T, PV); dK/dV kernel 8d (QK^T, dO V^T, P^T dO, dS^T Q);
+    dQ kernel 2d useful (dS K; its QK^T and dO V^T recompute is not counted)."""
+    per = {"fwd_bf16": 4 * d, "dkdv": 8 * d, "dq": 2 * d}.get(name)
+    return None if per is None else per * pairs * hq * batch
+
+
+def cpu_baseline(work, q, k, v, do, nrows, seed=0):
+    """Oracle (fp64 CPU) on a bounded sample of the same workload: forward
+    and dQ of `nrows` seeded (row, head) pairs of KV group 0."""
+    import torch
+
+    from oracle import oracle as orc
+    batch, L, M, hq, hkv, d = work
+    G = hq // hkv
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(0, 2 * L, size=nrows)
+    heads = rng.integers(0, G, size=nrows)
+    bsel = np.zeros(nrows, dtype=np.int32)
+
+    def host_full(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    hk, hv = host_full(k), host_full(v)
+    hq_ = np.zeros((batch, 2 * L, hq, d), dtype=np.uint16)
+    hdo = np.zeros((batch, 2 * L, hq, d), dtype=np.uint16)
+    idx = torch.as_tensor(pos, device=q.device)
+    hq_[0, pos, :G] = host_full(q[0, idx, :G])
+    hdo[0, pos, :G] = host_full(do[0, idx, :G])
+    p = orc.problem(batch, L, M, hq, hkv, d, bf16=True)
+    t0 = time.perf_counter()
+    orc.dq_rows(p, orc.keys(), orc.keys(), hq_, hk, hv, hdo, bsel, heads, pos)
+    dt = time.perf_counter() - t0
+    # visible keys of each sampled row (block-causal clean copy)
+    t = np.where(pos < L, pos, pos - L)
+    blk = t // M
+    nvis = np.where(pos < L, (blk + 1) * M, (blk + 1) * M)
+    flops = float(nvis.sum()) * 8 * d  # forward 4d + dQ part of the backward 4d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"fp64 forward + dQ of {nrows} seeded (row, head) pairs of KV group 0; "
+                      f"useful FLOPs 8*d per visible pair; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle sample size (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the hot path; runs on more than one GPU are not "
+              "part of this build (see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd import synth
+    from block_diffusion_lm_bdlm_amd.runner import WholeMask
+
+    dev = torch.device("cuda:0")
+    work = WORKLOADS[args.workload]
+    batch, L, M, hq, hkv, d = work
+    seed = synth.SEED_BASE + 2
+    n2 = 2 * L
+    print(f"[bench] generating inputs for {args.workload}", file=sys.stderr, flush=True)
+    q = synth.normal((batch, n2, hq, d), seed, "q", dev)
+    k = synth.normal((batch, n2, hkv, d), seed, "k", dev)
+    v = synth.normal((batch, n2, hkv, d), seed, "v", dev)
+    do = synth.normal((batch, n2, hq, d), seed, "do", dev)
+    wm = WholeMask(batch, L, M, hq, hkv, d)
+    ws_f = wm.workspace(False, dev)
+    ws_b = wm.workspace(True, dev)
+    grads = wm.alloc_grads(dev)
+    o = torch.empty(batch, n2, hq, d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(batch, n2, hq, dtype=torch.float32, device=dev)
+    L_ = L
+
+    def step():
+        for g_ in grads[:5]:
+            g_.zero_()
+        B.bdattn_fwd(wm.prob, wm.share, wm.kv, q[:, :L_], q[:, L_:], k[:, :L_], v[:, :L_], k[:, L_:],
+                     v[:, L_:], o, B.BDATTN_BF16, lse, ws_f)
+        dq, dkc, dvc, dkx, dvx, delta = grads
+        B.bdattn_bwd(wm.prob, wm.share, wm.kv, q[:, :L_], q[:, L_:], k[:, :L_], v[:, :L_], k[:, L_:],
+                     v[:, L_:], o, B.BDATTN_BF16, lse, do, delta, 0, dq, dkc, dvc, dkx, dvx, ws_b)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.bdattn_profile_read()  # drop anything recorded so far
+    B.bdattn_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    B.bdattn_profile_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = B.bdattn_profile_read()
+    print(f"[bench] {args.steps} steps, {ms:.2f} ms/step; kernels: "
+          + ", ".join(f"{n} {c}x {t / c:.3f} ms" for n, (c, t) in sorted(prof.items(), key=lambda x: -x[1][1])),
+          file=sys.stderr, flush=True)
+
+    pairs = visible_pairs(L, M)
+    useful = 14.0 * d * pairs * hq * batch
+    tflops = useful / (ms * 1e-3) / 1e12
+    # dominant kernel by time
+    dom = max(prof.items(), key=lambda kv_: kv_[1][1])
+    dom_name, (dom_cnt, dom_ms) = dom
+    dom_avg = dom_ms / dom_cnt
+    dflops = kernel_flops(dom_name, pairs, hq, batch, d)
+    roof = None
+    if dflops is not None:
+        ach = dflops / (dom_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(dom_avg, 3)}
+    cpu = None
+    if args.cpu_rows > 0:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(work, q, k, v, do, args.cpu_rows)
+    kernels = {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof.items()}
+    out = {
+        "metric": "useful attention TFLOP/s fwd+bwd at 64K (1 GPU); % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16 inputs, seeded",
+        "config": {"workload": args.workload, "batch": batch, "L": L, "positions": n2, "M": M, "hq": hq,
+                   "hkv": hkv, "d": d, "clean_mask": "block-causal", "parallelism": "single GPU"},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(batch * L / (ms * 1e-3), 1),
+        "useful_tflop_per_step": round(useful / 1e12, 3),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,7 @@ namespace {
 
 // ----------------------------------------------------------------- dQ
 template <int D>
-struct DqSmem {
+struct __attribute__((aligned(16))) DqSmem {
   static constexpr int KS = D + 8;
   static constexpr int TS = kBK + 8;
   uint16_t k[2][kBK * KS];
@@ -89,8 +89,7 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
   const float lse2 = A.lse2[crow_q];
   const float Dr = A.dc[crow_q];
   const RowBounds rb = row_bounds(P, S, r0 + rc);
-  KeyWalk w;
-  keywalk_build(P, S, r0, r0 + n - 1, w);
+  const KeyWalk w = keywalk_build(P, S, r0, r0 + n - 1);
   const float c2 = P.scale_log2;
 
   f32x16 dqacc[D / 32];
@@ -101,7 +100,8 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
     u32x4 kr[D / 32], vr[D / 32], tr[D / 32];
     {
       int32_t c, ri;
-      keywalk_at(w, 0, &c, &ri);
+      bool fu;
+      keywalk_at(w, 0, &c, &ri, &fu);
       dq_load<D>(A, P, b, g, c, tid, kr, vr, tr);
       dq_store<D>(sm, 0, tid, kr, vr, tr);
     }
@@ -109,10 +109,12 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
     for (int32_t t = 0; t < w.total; ++t) {
       const int buf = t & 1;
       int32_t c, ri;
-      keywalk_at(w, t, &c, &ri);
+      bool full;
+      keywalk_at(w, t, &c, &ri, &full);
       if (t + 1 < w.total) {
         int32_t cn, rn;
-        keywalk_at(w, t + 1, &cn, &rn);
+        bool fn;
+        keywalk_at(w, t + 1, &cn, &rn, &fn);
         dq_load<D>(A, P, b, g, cn, tid, kr, vr, tr);
       }
       f32x16 sacc[2], pacc[2];
@@ -127,7 +129,6 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
           pacc[kb] = mfma_bf16(ld16<bf16x8>(&sm.v[buf][off]), doreg[ks], pacc[kb]);
         }
       }
-      const bool full = keywalk_full(w, ri, c);
       int32_t vlo = c, vhi = c + kBK;
       if (!full) compact_range(P.k[ri], rb, clean, &vlo, &vhi);
       f16x8 dsf[2][2];
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(const Plan P, const DqArgs A
 
 // ----------------------------------------------------------------- dK / dV
 template <int D>
-struct DkdvSmem {
+struct __attribute__((aligned(16))) DkdvSmem {
   static constexpr int NS = D + 8;      // natural row stride
   static constexpr int TS = kBQB + 8;   // transposed row stride
   uint16_t q[2][kBQB * NS];
@@ -294,7 +295,10 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
   const int32_t total = per_head * P.G;
   const float c2 = P.scale_log2;
 
+  // walked back to front: the last rows are seen by every key tile, so the
+  // workgroups resident together start on the same rows and share them in L2
   auto locate = [&](int32_t t, int32_t* hsel, int32_t* sidx, int32_t* r0) {
+    t = total - 1 - t;
     *hsel = t / per_head;
     int32_t u = t - *hsel * per_head, j = 0;
     while (j + 1 < nseg && u >= sm.wcount[j]) { u -= sm.wcount[j]; ++j; }

@@ -22,7 +22,7 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int D>
-struct FwdSmem {
+struct __attribute__((aligned(16))) FwdSmem {
   static constexpr int KS = D + 8;    // K row stride (bf16 elements)
   static constexpr int VS = kBK + 8;  // V^T row stride (fp16 elements)
   uint16_t k[2][kBK * KS];
@@ -85,8 +85,7 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
   for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = ld16<bf16x8>(qp + ks * 16 + hh * 8);
 
   const RowBounds rb = row_bounds(P, S, r0 + rc);
-  KeyWalk w;
-  keywalk_build(P, S, r0, r0 + n - 1, w);
+  const KeyWalk w = keywalk_build(P, S, r0, r0 + n - 1);
 
   const float c2 = P.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
@@ -98,7 +97,8 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
     u32x4 kr[D / 32], vr[D / 32];
     {
       int32_t c, ri;
-      keywalk_at(w, 0, &c, &ri);
+      bool fu;
+      keywalk_at(w, 0, &c, &ri, &fu);
       fwd_load_tile<D>(A, P, b, g, c, tid, kr, vr);
       fwd_store_tile<D>(sm, 0, tid, kr, vr);
     }
@@ -106,10 +106,12 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
     for (int32_t t = 0; t < w.total; ++t) {
       const int buf = t & 1;
       int32_t c, ri;
-      keywalk_at(w, t, &c, &ri);
+      bool full;
+      keywalk_at(w, t, &c, &ri, &full);
       if (t + 1 < w.total) {
         int32_t cn, rn;
-        keywalk_at(w, t + 1, &cn, &rn);
+        bool fn;
+        keywalk_at(w, t + 1, &cn, &rn, &fn);
         fwd_load_tile<D>(A, P, b, g, cn, tid, kr, vr);
       }
       // S^T = K Q^T for two blocks of 32 keys
@@ -124,7 +126,6 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
           sacc[kb] = mfma_bf16(a, qreg[ks], sacc[kb]);
         }
       }
-      const bool full = keywalk_full(w, ri, c);
       if (!full) {
         int32_t vlo, vhi;
         compact_range(P.k[ri], rb, clean, &vlo, &vhi);
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const Plan P, const Fw
 // l+32 each own half of d), scores from LDS-staged fp32 K tiles on the
 // vector ALUs, the same online softmax, V accumulated in fp32.
 template <int D>
-struct F32Smem {
+struct __attribute__((aligned(16))) F32Smem {
   float k[kBK][D + 1];
   float v[kBK][D + 1];
 };
@@ -253,12 +254,12 @@ __device__ void fwd_f32_tile(const Plan& P, const FwdF32Args& A, F32Smem<D>& sm,
     o[t] = 0.f;
   }
   const RowBounds rb = row_bounds(P, S, r0 + rc);
-  KeyWalk w;
-  keywalk_build(P, S, r0, r0 + n - 1, w);
+  const KeyWalk w = keywalk_build(P, S, r0, r0 + n - 1);
   float m_run = -INFINITY, l_run = 0.f;
   for (int32_t t = 0; t < w.total; ++t) {
     int32_t c, ri;
-    keywalk_at(w, t, &c, &ri);
+    bool full;
+    keywalk_at(w, t, &c, &ri, &full);
     const KSeg K = P.k[ri];
     const TensorArg& KT = K.kind == KIND_CLEAN ? A.k_clean : A.k_corr;
     const TensorArg& VT = K.kind == KIND_CLEAN ? A.v_clean : A.v_corr;

@@ -21,7 +21,7 @@ namespace {
 constexpr int kPT = 64;  // rows per packing block
 
 template <int D>
-struct PackSmem {
+struct __attribute__((aligned(16))) PackSmem {
   uint16_t a[kPT][D + 8];  // bf16 rows (16-byte aligned)
   uint16_t b[kPT][D + 8];
 };

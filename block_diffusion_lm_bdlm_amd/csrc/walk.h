@@ -1,74 +1,77 @@
 // walk.h — key-tile walk of a query tile (forward and dQ kernels).
+//
+// A query tile visits, per key segment (at most three: two clean ranges and
+// the local corrupted keys), the key tiles any of its rows can see.  Fields
+// are named scalars so the walk lives in scalar registers.
 #pragma once
 
 #include "plan.h"
 
 namespace bd {
 
-// Key tiles a query tile visits: one slot per key segment (count 0 when the
-// segment holds no key the tile's rows see).  Constant-indexed so it stays
-// in registers.
+static_assert(kMaxKSeg == 3, "KeyWalk holds exactly three segments");
+
 struct KeyWalk {
   int32_t total;
-  int32_t start[kMaxKSeg], count[kMaxKSeg];
-  int32_t full_lo[kMaxKSeg], full_hi[kMaxKSeg];  // tiles inside [full_lo, full_hi) need no mask
+  int32_t s0, s1, s2;     // first tile (compact row) per segment
+  int32_t n0, n1, n2;     // tiles per segment
+  int32_t fl0, fl1, fl2;  // tiles inside [fl, fh) need no mask
+  int32_t fh0, fh1, fh2;
 };
 
-__device__ inline void keywalk_build(const Plan& P, const QSeg& S, int32_t r_first, int32_t r_last,
-                                     KeyWalk& w) {
+__device__ inline void keywalk_seg(const Plan& P, int32_t j, bool clean, const RowBounds& rf,
+                                   const RowBounds& rl, int32_t* s, int32_t* n, int32_t* fl,
+                                   int32_t* fh) {
+  *s = *n = *fl = *fh = 0;
+  if (j >= P.nk) return;
+  const KSeg K = P.k[j];
+  int32_t flo, fhi, llo, lhi;
+  compact_range(K, rf, clean, &flo, &fhi);
+  compact_range(K, rl, clean, &llo, &lhi);
+  if (lhi <= flo) return;
+  const int32_t a = K.c0 + ((flo - K.c0) / kBK) * kBK;
+  *s = a;
+  *n = (lhi - a + kBK - 1) / kBK;
+  *fl = llo;
+  *fh = fhi;
+}
+
+// Rows r_first..r_last of segment S are monotone in what they see, so the
+// first and last rows bound the walk.
+__device__ inline KeyWalk keywalk_build(const Plan& P, const QSeg& S, int32_t r_first, int32_t r_last) {
   const bool clean = S.kind == KIND_CLEAN;
   const RowBounds rf = row_bounds(P, S, r_first), rl = row_bounds(P, S, r_last);
-  w.total = 0;
-#pragma unroll
-  for (int32_t j = 0; j < kMaxKSeg; ++j) {
-    w.start[j] = 0;
-    w.count[j] = 0;
-    w.full_lo[j] = 0;
-    w.full_hi[j] = 0;
-    if (j < P.nk) {
-      const KSeg K = P.k[j];
-      int32_t flo, fhi, llo, lhi;
-      compact_range(K, rf, clean, &flo, &fhi);
-      compact_range(K, rl, clean, &llo, &lhi);
-      if (lhi > flo) {
-        const int32_t a = K.c0 + ((flo - K.c0) / kBK) * kBK;
-        w.start[j] = a;
-        w.count[j] = (lhi - a + kBK - 1) / kBK;
-        w.full_lo[j] = llo;
-        w.full_hi[j] = fhi;
-      }
-    }
-    w.total += w.count[j];
-  }
+  KeyWalk w;
+  keywalk_seg(P, 0, clean, rf, rl, &w.s0, &w.n0, &w.fl0, &w.fh0);
+  keywalk_seg(P, 1, clean, rf, rl, &w.s1, &w.n1, &w.fl1, &w.fh1);
+  keywalk_seg(P, 2, clean, rf, rl, &w.s2, &w.n2, &w.fl2, &w.fh2);
+  w.total = w.n0 + w.n1 + w.n2;
+  return w;
 }
 
-// Tile t of the walk -> compact start c and key segment j.
-__device__ inline void keywalk_at(const KeyWalk& w, int32_t t, int32_t* c, int32_t* j) {
-  int32_t sel = 0, u = t;
-#pragma unroll
-  for (int32_t k = 0; k < kMaxKSeg; ++k) {
-    if (sel == k && u >= w.count[k] && k + 1 < kMaxKSeg) {
-      u -= w.count[k];
-      sel = k + 1;
-    }
+// Tile t of the walk -> compact start c, segment j and whether it needs a mask.
+__device__ inline void keywalk_at(const KeyWalk& w, int32_t t, int32_t* c, int32_t* j, bool* full) {
+  int32_t start, lo, hi;
+  if (t < w.n0) {
+    *j = 0;
+    start = w.s0;
+    lo = w.fl0;
+    hi = w.fh0;
+  } else if (t < w.n0 + w.n1) {
+    t -= w.n0;
+    *j = 1;
+    start = w.s1;
+    lo = w.fl1;
+    hi = w.fh1;
+  } else {
+    t -= w.n0 + w.n1;
+    *j = 2;
+    start = w.s2;
+    lo = w.fl2;
+    hi = w.fh2;
   }
-  int32_t st = w.start[0];
-#pragma unroll
-  for (int32_t k = 1; k < kMaxKSeg; ++k)
-    if (sel == k) st = w.start[k];
-  *j = sel;
-  *c = st + u * kBK;
-}
-
-__device__ inline bool keywalk_full(const KeyWalk& w, int32_t j, int32_t c) {
-  int32_t lo = w.full_lo[0], hi = w.full_hi[0];
-#pragma unroll
-  for (int32_t k = 1; k < kMaxKSeg; ++k)
-    if (j == k) {
-      lo = w.full_lo[k];
-      hi = w.full_hi[k];
-    }
-  return c >= lo && c + kBK <= hi;
+  *c = start + t * kBK;
+  *full = *c >= lo && *c + kBK <= hi;
 }
 
 }  // namespace bd
