@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["bdattn.cpp", "fwd.hip", "pack.hip", "bwd.hip", "merge.hip"]
+SOURCES = ["bdattn.cpp", "fwd.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
 ARCH = os.environ.get("BDATTN_ARCH", "gfx950")
 
 

@@ -27,7 +27,7 @@ constexpr int kMaxKSeg = 3;
 constexpr int kBQ = 128;     // query rows per tile (forward, dQ)
 constexpr int kBK = 64;      // keys per tile (forward, dQ)
 constexpr int kBKB = 128;    // keys per tile (dK/dV)
-constexpr int kBQB = 32;     // query rows per step (dK/dV)
+constexpr int kBQB = 64;     // query rows per step (dK/dV)
 constexpr int kAlign = 128;  // compact key segments start at multiples of this
 constexpr int kXCD = 8;      // MI355X accelerator complex dies
 
