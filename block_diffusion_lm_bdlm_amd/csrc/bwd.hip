@@ -118,13 +118,16 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
       for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = f32x16{};
         pacc[kb] = f32x16{};
+      }
+      // consecutive products feed different accumulators (independent chains)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
           const int off = (kb * 32 + ql) * DqSmem<D>::KS + ks * 16 + hh * 8;
           sacc[kb] = mfma_bf16(ld16<bf16x8>(&sm.k[buf][off]), qreg[ks], sacc[kb]);
           pacc[kb] = mfma_bf16(ld16<bf16x8>(&sm.v[buf][off]), doreg[ks], pacc[kb]);
         }
-      }
       int32_t vlo = c, vhi = c + kBK;
       if (!full) compact_range(P.k[ri], rb, clean, &vlo, &vhi);
       f16x8 dsf[2][2];
@@ -139,11 +142,11 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
         }
       // dQ^T += K^T dS^T
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-          for (int ss = 0; ss < 2; ++ss) {
+          for (int db = 0; db < D / 32; ++db) {
             const f16x8 a =
                 ld16<f16x8>(&sm.kt[buf][(db * 32 + ql) * DqSmem<D>::TS + kb * 32 + ss * 16 + hh * 8]);
             dqacc[db] = mfma_f16(a, dsf[kb][ss], dqacc[db]);

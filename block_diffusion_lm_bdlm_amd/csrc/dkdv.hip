@@ -7,12 +7,18 @@
 // contributions from every later block, section "CSBP：BP 管损坏块，CP 管干净
 // 上下文").
 //
-// A workgroup owns 128 keys of one KV head, 32 per wave: K and V sit in
-// registers as B operands, dK^T and dV^T accumulate in registers, so every
-// key has exactly one writer and no atomics are needed.  The workgroup walks
-// every query row (of every query head of the group) that sees its keys, in
-// steps of 64 rows staged through LDS (natural Q, dO for S = Q K^T and
-// dP = dO V^T; transposed fp16 Q^T, dO^T for the contractions over rows).
+// A workgroup owns 128 keys of one KV head and runs 8 waves, two per SIMD,
+// in pairs that own the same 32 keys:
+//   S-wave: K in registers; S = Q K^T, P = exp(S - LSE) (masked), writes P
+//           to LDS, accumulates dV^T += dO^T P.
+//   P-wave: V in registers; dP = dO V^T, reads P, dS = P (dP - D),
+//           accumulates dK^T += Q^T dS.
+// Each key has exactly one writer per gradient, so no atomics are needed,
+// and the two waves of a SIMD overlap one's vector work with the other's
+// matrix work.  The workgroup walks every query row (of every query head of
+// the group) that sees its keys, in steps of 64 rows staged through LDS
+// (natural Q, dO for S and dP; transposed fp16 Q^T, dO^T for the
+// contractions over rows).
 // The walk runs back to front: the last rows are seen by every key tile, so
 // the workgroups resident on one XCD start on the same rows and share them
 // through L2.  Each step stages per-row visibility bounds next to LSE and D,
@@ -41,6 +47,8 @@ struct __attribute__((aligned(16))) DkdvSmem {
   float dc[2][kBQB];
   int32_t vlo[2][kBQB];  // row sees key sources [vlo, vhi) of this key tile's segment
   int32_t vhi[2][kBQB];
+  // P from each S-wave to its P-wave, in the MFMA C-tile order of each lane
+  _Float16 xchg[4][kNB][64][16];
   // steps of the walk: segment s contributes wcount[s] steps from row wfirst[s]
   int32_t wseg[kMaxQSeg], wfirst[kMaxQSeg], wcount[kMaxQSeg];
   int32_t wn, wper;
@@ -51,28 +59,34 @@ struct StepPos {
   int32_t hs, j, u;
 };
 
+constexpr int kThreads = 512;  // 8 waves
+
+// Prefetch of one step, in two halves so each is live for half a step:
+// A = natural Q, dO and the per-row data; B = transposed Q^T, dO^T.
 template <int D>
-struct Stage {
-  static constexpr int NCH = kBQB * D / 8 / 256;  // 16-byte chunks per thread per tensor
-  u32x4 r[4 * NCH];
+struct StageA {
+  static constexpr int NCH = kBQB * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
+  u32x4 r[2 * NCH];
   float l2, dd;
   int32_t lo, hi;
 };
+template <int D>
+struct StageB {
+  static constexpr int NCH = kBQB * D / 8 / kThreads;
+  u32x4 r[2 * NCH];
+};
 
 template <int D>
-__device__ inline void stage_load(const DkdvArgs& A, const Plan& P, const KSeg& K, const QSeg& S, int64_t hb,
-                                  int32_t r0, int tid, Stage<D>& st) {
-  constexpr int NCH = Stage<D>::NCH;
+__device__ inline void stage_load_a(const DkdvArgs& A, const Plan& P, const KSeg& K, const QSeg& S, int64_t hb,
+                                    int32_t r0, int tid, StageA<D>& st) {
+  constexpr int NCH = StageA<D>::NCH;
   const int32_t cq = S.tile0 * kBQ + r0;  // compact row of the step's first row
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int ch = tid + 256 * j;
+    const int ch = tid + kThreads * j;
     const int row = ch / (D / 8), dcol = ch % (D / 8);
     st.r[j] = ldg16(A.qn + (hb * P.nqc + cq + row) * D + dcol * 8);
     st.r[NCH + j] = ldg16(A.don + (hb * P.nqc + cq + row) * D + dcol * 8);
-    const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
-    st.r[2 * NCH + j] = ldg16(A.qt + (hb * D + d) * P.nqc + cq + sc * 8);
-    st.r[3 * NCH + j] = ldg16(A.dot + (hb * D + d) * P.nqc + cq + sc * 8);
   }
   if (tid < kBQB) {
     st.l2 = A.lse2[hb * P.nqc + cq + tid];
@@ -93,17 +107,28 @@ __device__ inline void stage_load(const DkdvArgs& A, const Plan& P, const KSeg& 
 }
 
 template <int D>
-__device__ inline void stage_store(DkdvSmem<D>& sm, int buf, int tid, const Stage<D>& st) {
-  constexpr int NCH = Stage<D>::NCH;
+__device__ inline void stage_load_b(const DkdvArgs& A, const Plan& P, const QSeg& S, int64_t hb, int32_t r0,
+                                    int tid, StageB<D>& st) {
+  constexpr int NCH = StageB<D>::NCH;
+  const int32_t cq = S.tile0 * kBQ + r0;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int ch = tid + 256 * j;
+    const int ch = tid + kThreads * j;
+    const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
+    st.r[j] = ldg16(A.qt + (hb * D + d) * P.nqc + cq + sc * 8);
+    st.r[NCH + j] = ldg16(A.dot + (hb * D + d) * P.nqc + cq + sc * 8);
+  }
+}
+
+template <int D>
+__device__ inline void stage_store_a(DkdvSmem<D>& sm, int buf, int tid, const StageA<D>& st) {
+  constexpr int NCH = StageA<D>::NCH;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int ch = tid + kThreads * j;
     const int row = ch / (D / 8), dcol = ch % (D / 8);
     *reinterpret_cast<u32x4*>(&sm.q[buf][row * DkdvSmem<D>::NS + dcol * 8]) = st.r[j];
     *reinterpret_cast<u32x4*>(&sm.dO[buf][row * DkdvSmem<D>::NS + dcol * 8]) = st.r[NCH + j];
-    const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
-    *reinterpret_cast<u32x4*>(&sm.qt[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[2 * NCH + j];
-    *reinterpret_cast<u32x4*>(&sm.dot[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[3 * NCH + j];
   }
   if (tid < kBQB) {
     sm.lse2[buf][tid] = st.l2;
@@ -113,17 +138,27 @@ __device__ inline void stage_store(DkdvSmem<D>& sm, int buf, int tid, const Stag
   }
 }
 
-// One 32-row block's probabilities and dS in fp16, packed as the two B
-// operands (k-steps) of the contraction over rows.
-__device__ __forceinline__ void block_softmax(bool full, const f32x16& sacc, const f32x16& pacc,
-                                              const float* lse2, const float* dc, const int32_t* vlo,
-                                              const int32_t* vhi, int hh, int32_t mysrc, float c2,
-                                              f16x8 (&pf)[2], f16x8 (&dsf)[2]) {
+template <int D>
+__device__ inline void stage_store_b(DkdvSmem<D>& sm, int buf, int tid, const StageB<D>& st) {
+  constexpr int NCH = StageB<D>::NCH;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int ch = tid + kThreads * j;
+    const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
+    *reinterpret_cast<u32x4*>(&sm.qt[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[j];
+    *reinterpret_cast<u32x4*>(&sm.dot[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[NCH + j];
+  }
+}
+
+// S-wave, one 32-row block: P = exp2(S c2 - LSE2) on visible pairs, in fp16,
+// packed as the two B operands (k-steps) of the contraction over rows.
+__device__ __forceinline__ void block_p(bool full, const f32x16& sacc, const float* lse2, const int32_t* vlo,
+                                        const int32_t* vhi, int hh, int32_t mysrc, float c2,
+                                        f16x8 (&pf)[2]) {
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const int rb = i4 * 8 + hh * 4;  // C rows rb .. rb+3 of the block
     const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + rb);
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dc + rb);
     // full steps: every row sees every key, [INT_MIN, INT_MAX) admits all
     int4 lo4 = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, hi4 = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
     if (!full) {
@@ -136,51 +171,170 @@ __device__ __forceinline__ void block_softmax(bool full, const f32x16& sacc, con
     for (int e = 0; e < 4; ++e) {
       const int i = i4 * 4 + e;
       const float x = (mysrc >= los[e] && mysrc < his[e]) ? fmaf(sacc[i], c2, -l4[e]) : -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(x);
-      pf[i >> 3][i & 7] = (_Float16)p;
-      dsf[i >> 3][i & 7] = (_Float16)(p * (pacc[i] - d4[e]));
+      pf[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(x);
     }
   }
 }
 
-// One step: 64 query rows staged in LDS buffer BUF against this wave's 32 keys.
+// S-wave, first half of a step: S = Q K^T and P (kept in pf, copied to LDS).
 template <int D>
-__device__ __forceinline__ void dkdv_step(DkdvSmem<D>& sm, bool full, int BUF, int ql, int hh, int32_t mysrc, float c2,
-                                          const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
-                                          f32x16 (&dkacc)[D / 32], f32x16 (&dvacc)[D / 32]) {
-  constexpr int NS = DkdvSmem<D>::NS, TS = DkdvSmem<D>::TS;
+__device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, bool full, int BUF, int kw, int lane, int ql, int hh,
+                                          int32_t mysrc, float c2, const bf16x8 (&kreg)[D / 16],
+                                          f16x8 (&pf)[kNB][2]) {
+  constexpr int NS = DkdvSmem<D>::NS;
   const uint16_t* qb = &sm.q[BUF][ql * NS + hh * 8];
-  const uint16_t* ob = &sm.dO[BUF][ql * NS + hh * 8];
-  const _Float16* qtb = &sm.qt[BUF][ql * TS + hh * 8];
-  const _Float16* otb = &sm.dot[BUF][ql * TS + hh * 8];
+  f32x16 sacc[kNB];
+#pragma unroll
+  for (int blk = 0; blk < kNB; ++blk) sacc[blk] = f32x16{};
+  // consecutive products feed different accumulators (independent chains)
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk)
+      sacc[blk] = mfma_bf16(ld16<bf16x8>(qb + blk * 32 * NS + ks * 16), kreg[ks], sacc[blk]);
 #pragma unroll
   for (int blk = 0; blk < kNB; ++blk) {
-    // S = Q K^T, dP = dO V^T for the block's 32 rows
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    block_p(full, sacc[blk], &sm.lse2[BUF][blk * 32], &sm.vlo[BUF][blk * 32], &sm.vhi[BUF][blk * 32], hh,
+            mysrc, c2, pf[blk]);
+    *reinterpret_cast<f16x8*>(&sm.xchg[kw][blk][lane][0]) = pf[blk][0];
+    *reinterpret_cast<f16x8*>(&sm.xchg[kw][blk][lane][8]) = pf[blk][1];
+  }
+}
+
+// S-wave, second half: dV^T += dO^T P.
+template <int D>
+__device__ __forceinline__ void s_phase_b(DkdvSmem<D>& sm, int BUF, int ql, int hh, const f16x8 (&pf)[kNB][2],
+                                          f32x16 (&dvacc)[D / 32]) {
+  constexpr int TS = DkdvSmem<D>::TS;
+  const _Float16* otb = &sm.dot[BUF][ql * TS + hh * 8];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      sacc = mfma_bf16(ld16<bf16x8>(qb + blk * 32 * NS + ks * 16), kreg[ks], sacc);
-      pacc = mfma_bf16(ld16<bf16x8>(ob + blk * 32 * NS + ks * 16), vreg[ks], pacc);
-    }
-    f16x8 pf[2], dsf[2];
-    block_softmax(full, sacc, pacc, &sm.lse2[BUF][blk * 32], &sm.dc[BUF][blk * 32], &sm.vlo[BUF][blk * 32],
-                        &sm.vhi[BUF][blk * 32], hh, mysrc, c2, pf, dsf);
-    // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the block's 32 rows)
+  for (int blk = 0; blk < kNB; ++blk)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const int off = db * 32 * TS + blk * 32 + ss * 16;
-        dvacc[db] = mfma_f16(ld16<f16x8>(otb + off), pf[ss], dvacc[db]);
-        dkacc[db] = mfma_f16(ld16<f16x8>(qtb + off), dsf[ss], dkacc[db]);
+      for (int db = 0; db < D / 32; ++db)
+        dvacc[db] = mfma_f16(ld16<f16x8>(otb + db * 32 * TS + blk * 32 + ss * 16), pf[blk][ss], dvacc[db]);
+}
+
+// P-wave, first half of a step: dP = dO V^T.
+template <int D>
+__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int BUF, int ql, int hh, const bf16x8 (&vreg)[D / 16],
+                                          f32x16 (&pacc)[kNB]) {
+  constexpr int NS = DkdvSmem<D>::NS;
+  const uint16_t* ob = &sm.dO[BUF][ql * NS + hh * 8];
+#pragma unroll
+  for (int blk = 0; blk < kNB; ++blk) pacc[blk] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk)
+      pacc[blk] = mfma_bf16(ld16<bf16x8>(ob + blk * 32 * NS + ks * 16), vreg[ks], pacc[blk]);
+}
+
+// P-wave, second half: dS = P (dP - D) with P from its S-wave, dK^T += Q^T dS.
+template <int D>
+__device__ __forceinline__ void p_phase_b(DkdvSmem<D>& sm, int BUF, int kw, int lane, int ql, int hh,
+                                          const f32x16 (&pacc)[kNB], f32x16 (&dkacc)[D / 32]) {
+  constexpr int TS = DkdvSmem<D>::TS;
+  const _Float16* qtb = &sm.qt[BUF][ql * TS + hh * 8];
+#pragma unroll
+  for (int blk = 0; blk < kNB; ++blk) {
+    const f16x8 p0 = ld16<f16x8>(&sm.xchg[kw][blk][lane][0]);
+    const f16x8 p1 = ld16<f16x8>(&sm.xchg[kw][blk][lane][8]);
+    f16x8 dsf[2];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dc[BUF][blk * 32 + i4 * 8 + hh * 4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i4 * 4 + e;
+        const float p = (float)((i < 8) ? p0[i & 7] : p1[i & 7]);
+        dsf[i >> 3][i & 7] = (_Float16)(p * (pacc[blk][i] - d4[e]));
       }
+    }
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        dkacc[db] = mfma_f16(ld16<f16x8>(qtb + db * 32 * TS + blk * 32 + ss * 16), dsf[ss], dkacc[db]);
+  }
+}
+
+// The query walk of one role.  S-waves and P-waves run the same sequence of
+// barriers: two per step (after P is exchanged, after the prefetch lands).
+template <int D, bool S_WAVE>
+__device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, const KSeg& K, int b,
+                                          int g, int32_t kvalid, int32_t kt1, int tid, int kw, int lane, int ql,
+                                          int hh, int32_t mysrc, int32_t nseg, int32_t total,
+                                          const bf16x8 (&kvreg)[D / 16], f32x16 (&acc)[D / 32]) {
+  const float c2 = P.scale_log2;
+  // walk back to front: last head, last segment, last step first
+  StepPos cur{P.G - 1, nseg - 1, sm.wcount[nseg - 1] - 1};
+  auto advance = [&](StepPos p) {
+    if (--p.u < 0) {
+      if (--p.j < 0) {
+        p.j = nseg - 1;
+        --p.hs;
+      }
+      p.u = sm.wcount[p.j] - 1;
+    }
+    return p;
+  };
+  auto hb_of = [&](const StepPos& p) { return (int64_t)(b * P.hq + g * P.G + p.hs); };
+  StageA<D> sa;
+  StageB<D> sb;
+  {
+    const int32_t r0 = sm.wfirst[cur.j] + cur.u * kBQB;
+    stage_load_a<D>(A, P, K, P.q[sm.wseg[cur.j]], hb_of(cur), r0, tid, sa);
+    stage_load_b<D>(A, P, P.q[sm.wseg[cur.j]], hb_of(cur), r0, tid, sb);
+    stage_store_a<D>(sm, 0, tid, sa);
+    stage_store_b<D>(sm, 0, tid, sb);
+  }
+  __syncthreads();
+  for (int32_t t = 0; t < total; ++t) {
+    const int BUF = t & 1;
+    const int32_t si = sm.wseg[cur.j];
+    const int32_t r0 = sm.wfirst[cur.j] + cur.u * kBQB;
+    const bool more = t + 1 < total;
+    StepPos nxt = cur;
+    int32_t sn = si, rn = 0;
+    if (more) {
+      nxt = advance(cur);
+      sn = sm.wseg[nxt.j];
+      rn = sm.wfirst[nxt.j] + nxt.u * kBQB;
+      stage_load_a<D>(A, P, K, P.q[sn], hb_of(nxt), rn, tid, sa);
+    }
+    if constexpr (S_WAVE) {
+      // no mask when every row of the step exists and sees every key of the tile
+      bool full = false;
+      if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= P.q[si].nrows)
+        full = row_bounds(P, P.q[si], r0).hi_clean >= kt1;
+      f16x8 pf[kNB][2];
+      s_phase_a<D>(sm, full, BUF, kw, lane, ql, hh, mysrc, c2, kvreg, pf);
+      if (more) stage_store_a<D>(sm, BUF ^ 1, tid, sa);
+      __syncthreads();  // P visible to the P-waves
+      if (more) stage_load_b<D>(A, P, P.q[sn], hb_of(nxt), rn, tid, sb);
+      s_phase_b<D>(sm, BUF, ql, hh, pf, acc);
+    } else {
+      f32x16 pacc[kNB];
+      p_phase_a<D>(sm, BUF, ql, hh, kvreg, pacc);
+      if (more) stage_store_a<D>(sm, BUF ^ 1, tid, sa);
+      __syncthreads();  // P from the S-waves
+      if (more) stage_load_b<D>(A, P, P.q[sn], hb_of(nxt), rn, tid, sb);
+      p_phase_b<D>(sm, BUF, kw, lane, ql, hh, pacc, acc);
+    }
+    if (more) stage_store_b<D>(sm, BUF ^ 1, tid, sb);
+    __syncthreads();
+    cur = nxt;
   }
 }
 
 template <int D>
 __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int b, int g, int32_t ktile) {
-  static_assert(kBQB * D / 8 >= 256 && (kBQB * D / 8) % 256 == 0, "chunking");
+  static_assert(kBQB * D / 8 >= kThreads && (kBQB * D / 8) % kThreads == 0, "chunking");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int kw = wave & 3;            // which 32 keys of the tile
+  const bool s_wave = wave < 4;       // S-wave (dV) or P-wave (dK)
   int32_t kseg, koff;
   ktile_locate(P, ktile, &kseg, &koff);
   const KSeg K = P.k[kseg];
@@ -188,25 +342,21 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
   const int32_t kt0 = K.t0 + koff;                 // first source row
   const int32_t kt1 = kt0 + kvalid;
   const int32_t c = K.c0 + koff;                   // compact start
-  const int32_t mykey = wave * 32 + ql;
+  const int32_t mykey = kw * 32 + ql;
   const bool key_ok = mykey < kvalid;
   const int32_t mysrc = key_ok ? kt0 + mykey : INT_MIN;
 
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // this wave's 32 keys as B operands: K (S-wave) or V (P-wave)
+  bf16x8 kvreg[D / 16];
   {
-    const int64_t nb = ((int64_t)(b * P.hkv + g) * P.nkc + c + wave * 32 + ql) * D;
+    const uint16_t* src = s_wave ? A.kn : A.vn;
+    const int64_t nb = ((int64_t)(b * P.hkv + g) * P.nkc + c + kw * 32 + ql) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kreg[ks] = ld16<bf16x8>(A.kn + nb + ks * 16 + hh * 8);
-      vreg[ks] = ld16<bf16x8>(A.vn + nb + ks * 16 + hh * 8);
-    }
+    for (int ks = 0; ks < D / 16; ++ks) kvreg[ks] = ld16<bf16x8>(src + nb + ks * 16 + hh * 8);
   }
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 acc[D / 32];  // dV^T (S-wave) or dK^T (P-wave)
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dkacc[db] = f32x16{};
-    dvacc[db] = f32x16{};
-  }
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   if (tid == 0) {
     int32_t nseg = 0, per = 0;
@@ -228,84 +378,39 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
   __syncthreads();
   const int32_t nseg = sm.wn;
   const int32_t total = sm.wper * P.G;
-  const float c2 = P.scale_log2;
 
   if (total > 0) {
-    // walk back to front: last head, last segment, last step first
-    StepPos cur{P.G - 1, nseg - 1, sm.wcount[nseg - 1] - 1};
-    auto advance = [&](StepPos p) {
-      if (--p.u < 0) {
-        if (--p.j < 0) {
-          p.j = nseg - 1;
-          --p.hs;
-        }
-        p.u = sm.wcount[p.j] - 1;
-      }
-      return p;
-    };
-    auto hb_of = [&](const StepPos& p) { return (int64_t)(b * P.hq + g * P.G + p.hs); };
-    Stage<D> st;
-    {
-      const QSeg& S = P.q[sm.wseg[cur.j]];
-      stage_load<D>(A, P, K, S, hb_of(cur), sm.wfirst[cur.j] + cur.u * kBQB, tid, st);
-      stage_store<D>(sm, 0, tid, st);
-    }
-    __syncthreads();
-    // each step: prefetch the next one into registers, compute from LDS
-    // buffer t & 1, then move the prefetch into the other buffer
-    for (int32_t t = 0; t < total; ++t) {
-      const int BUF = t & 1;
-      const QSeg S = P.q[sm.wseg[cur.j]];
-      const int32_t r0 = sm.wfirst[cur.j] + cur.u * kBQB;
-      StepPos nxt = cur;
-      if (t + 1 < total) {
-        nxt = advance(cur);
-        const QSeg& Sn = P.q[sm.wseg[nxt.j]];
-        stage_load<D>(A, P, K, Sn, hb_of(nxt), sm.wfirst[nxt.j] + nxt.u * kBQB, tid, st);
-      }
-      // no mask when every row of the step exists and sees every key of the tile
-      bool full = false;
-      if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= S.nrows)
-        full = row_bounds(P, S, r0).hi_clean >= kt1;
-      dkdv_step<D>(sm, full, BUF, ql, hh, mysrc, c2, kreg, vreg, dkacc, dvacc);
-      if (t + 1 < total) stage_store<D>(sm, BUF ^ 1, tid, st);
-      __syncthreads();
-      cur = nxt;
-    }
+    if (s_wave)
+      dkdv_walk<D, true>(P, A, sm, K, b, g, kvalid, kt1, tid, kw, lane, ql, hh, mysrc, nseg, total, kvreg, acc);
+    else
+      dkdv_walk<D, false>(P, A, sm, K, b, g, kvalid, kt1, tid, kw, lane, ql, hh, mysrc, nseg, total, kvreg, acc);
   }
   if (key_ok) {
-    float *dk, *dv;
+    float* dst;
     int64_t rowoff;
     if (K.kind == KIND_CLEAN) {
-      dk = A.dk_clean;
-      dv = A.dv_clean;
+      dst = s_wave ? A.dv_clean : A.dk_clean;
       rowoff = (((int64_t)b * P.L + mysrc) * P.hkv + g) * D;
     } else {
-      dk = A.dk_corr;
-      dv = A.dv_corr;
+      dst = s_wave ? A.dv_corr : A.dk_corr;
       rowoff = (((int64_t)b * P.n_corr_rows + mysrc) * P.hkv + g) * D;
     }
+    const float f = s_wave ? 1.f : P.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; i += 4) {
-        const int d = db * 32 + crow(i, hh);
-        f32x4* pk = reinterpret_cast<f32x4*>(dk + rowoff + d);
-        f32x4* pv = reinterpret_cast<f32x4*>(dv + rowoff + d);
-        f32x4 ck = *pk, cv = *pv;
+        f32x4* pd = reinterpret_cast<f32x4*>(dst + rowoff + db * 32 + crow(i, hh));
+        f32x4 cur4 = *pd;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ck[e] += P.scale * dkacc[db][i + e];
-          cv[e] += dvacc[db][i + e];
-        }
-        *pk = ck;
-        *pv = cv;
+        for (int e = 0; e < 4; ++e) cur4[e] += f * acc[db][i + e];
+        *pd = cur4;
       }
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(const Plan P, const DkdvArgs A) {
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const Plan P, const DkdvArgs A) {
   __shared__ DkdvSmem<D> sm;
   const WgK wg = decode_wg_k(P, blockIdx.x);
   dkdv_tile<D>(P, A, sm, wg.b, wg.g, wg.tile_a);
@@ -320,9 +425,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const Plan P, const DkdvAr
 hipError_t launch_dkdv(const Plan& P, const DkdvArgs& a, hipStream_t s) {
   if (P.nwg_k == 0) return hipSuccess;
   if (P.d == 128)
-    hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)P.nwg_k), dim3(256), 0, s, P, a);
+    hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)P.nwg_k), dim3(kThreads), 0, s, P, a);
   else
-    hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)P.nwg_k), dim3(256), 0, s, P, a);
+    hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)P.nwg_k), dim3(kThreads), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -117,15 +117,16 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       // S^T = K Q^T for two blocks of 32 keys
       f32x16 sacc[2];
       const uint16_t* kbase = sm.k[buf];
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+      // consecutive products feed different accumulators (independent chains)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
+      for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 a = ld16<bf16x8>(kbase + (kb * 32 + ql) * FwdSmem<D>::KS + ks * 16 + hh * 8);
           sacc[kb] = mfma_bf16(a, qreg[ks], sacc[kb]);
         }
-      }
       if (!full) {
         int32_t vlo, vhi;
         compact_range(P.k[ri], rb, clean, &vlo, &vhi);
@@ -166,11 +167,11 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       // O^T += V^T P^T
       const _Float16* vbase = sm.v[buf];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-          for (int ss = 0; ss < 2; ++ss) {
+          for (int db = 0; db < D / 32; ++db) {
             const f16x8 a =
                 ld16<f16x8>(vbase + (db * 32 + ql) * FwdSmem<D>::VS + kb * 32 + ss * 16 + hh * 8);
             oacc[db] = mfma_f16(a, pf[kb][ss], oacc[db]);
