@@ -11,6 +11,7 @@ Useful FLOPs count visible (query, key) pairs only: 4 d per pair forward and
 clean copy.  Printed as one JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,42 @@ WORKLOADS = {
     "bdlm_L8K_M32_b2_h16kv8_d128": (2, 8192, 32, 16, 8, 128),
 }
 DEFAULT = "bdlm_L64K_M32_h40kv8_d128"
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, scaled by the copy-kernel calibration; None when absent or
+    when the kernel's sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or sources_sha(rec["sources"]) != rec["sha256"]:
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def calibrate_copy(nbytes):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
 def visible_pairs(L, M):
@@ -86,8 +123,13 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle sample size (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (0: skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the hot path; runs on more than one GPU are not "
               "part of this build (see DESIGN.md, 'How the path would shard').", file=sys.stderr)
@@ -158,7 +200,7 @@ def main():
     if dflops is not None:
         ach = dflops / (dom_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom_name),
                 "avg_ms": round(dom_avg, 3)}
     cpu = None
     if args.cpu_rows > 0:

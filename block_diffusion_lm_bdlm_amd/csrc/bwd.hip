@@ -41,12 +41,12 @@ __device__ inline void dq_load(const DqArgs& A, const Plan& P, int b, int g, int
     kr[j] = ldg16(A.kn + nb + key * D + dc * 8);
     vr[j] = ldg16(A.vn + nb + key * D + dc * 8);
   }
-  const _Float16* tb = A.kt + (int64_t)(b * P.hkv + g) * D * P.nkc + c;
+  const _Float16* tb = A.kt + (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // [D][64] tile
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
     const int ch = tid + 256 * j;
     const int d = ch / (kBK / 8), kc = ch % (kBK / 8);
-    tr[j] = ldg16(tb + (int64_t)d * P.nkc + kc * 8);
+    tr[j] = ldg16(tb + d * kBK + kc * 8);
   }
 }
 

@@ -19,9 +19,9 @@
 // the group) that sees its keys, in steps of 64 rows staged through LDS
 // (natural Q, dO for S and dP; transposed fp16 Q^T, dO^T for the
 // contractions over rows).
-// The walk runs back to front: the last rows are seen by every key tile, so
-// the workgroups resident on one XCD start on the same rows and share them
-// through L2.  Each step stages per-row visibility bounds next to LSE and D,
+// The walk runs back to front by position (all heads of the group at each
+// position): the last rows are seen by every key tile, so the workgroups
+// resident on one XCD stay on the same rows and share them through L2.  Each step stages per-row visibility bounds next to LSE and D,
 // so a step that straddles the mask boundary needs no division per element.
 #include <climits>
 #include <type_traits>
@@ -54,9 +54,10 @@ struct __attribute__((aligned(16))) DkdvSmem {
   int32_t wn, wper;
 };
 
-// Position of the walk: query head (within the group), walk segment, step.
+// Position of the walk: k-th step from the end of walk segment j, query head
+// hs within the group.
 struct StepPos {
-  int32_t hs, j, u;
+  int32_t k, j, hs;
 };
 
 constexpr int kThreads = 512;  // 8 waves
@@ -115,8 +116,9 @@ __device__ inline void stage_load_b(const DkdvArgs& A, const Plan& P, const QSeg
   for (int j = 0; j < NCH; ++j) {
     const int ch = tid + kThreads * j;
     const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
-    st.r[j] = ldg16(A.qt + (hb * D + d) * P.nqc + cq + sc * 8);
-    st.r[NCH + j] = ldg16(A.dot + (hb * D + d) * P.nqc + cq + sc * 8);
+    const int64_t t = hb * D * P.nqc + (int64_t)cq * D + d * kBQB + sc * 8;  // [D][64] tile of row cq
+    st.r[j] = ldg16(A.qt + t);
+    st.r[NCH + j] = ldg16(A.dot + t);
   }
 }
 
@@ -268,23 +270,28 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
                                           int hh, int32_t mysrc, int32_t nseg, int32_t total,
                                           const bf16x8 (&kvreg)[D / 16], f32x16 (&acc)[D / 32]) {
   const float c2 = P.scale_log2;
-  // walk back to front: last head, last segment, last step first
-  StepPos cur{P.G - 1, nseg - 1, sm.wcount[nseg - 1] - 1};
+  // Walk back to front by position: the k-th step from the end of every
+  // segment, for every query head, then step k+1.  Every key tile's rows
+  // run to the end of each segment, so the workgroups resident together on
+  // an XCD visit the same rows at the same time and share them through L2.
+  StepPos cur{0, nseg - 1, P.G - 1};
   auto advance = [&](StepPos p) {
-    if (--p.u < 0) {
+    if (--p.hs >= 0) return p;
+    p.hs = P.G - 1;
+    do {
       if (--p.j < 0) {
         p.j = nseg - 1;
-        --p.hs;
+        ++p.k;
       }
-      p.u = sm.wcount[p.j] - 1;
-    }
+    } while (p.k >= sm.wcount[p.j]);
     return p;
   };
+  auto row_of = [&](const StepPos& p) { return sm.wfirst[p.j] + (sm.wcount[p.j] - 1 - p.k) * kBQB; };
   auto hb_of = [&](const StepPos& p) { return (int64_t)(b * P.hq + g * P.G + p.hs); };
   StageA<D> sa;
   StageB<D> sb;
   {
-    const int32_t r0 = sm.wfirst[cur.j] + cur.u * kBQB;
+    const int32_t r0 = row_of(cur);
     stage_load_a<D>(A, P, K, P.q[sm.wseg[cur.j]], hb_of(cur), r0, tid, sa);
     stage_load_b<D>(A, P, P.q[sm.wseg[cur.j]], hb_of(cur), r0, tid, sb);
     stage_store_a<D>(sm, 0, tid, sa);
@@ -294,14 +301,14 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
   for (int32_t t = 0; t < total; ++t) {
     const int BUF = t & 1;
     const int32_t si = sm.wseg[cur.j];
-    const int32_t r0 = sm.wfirst[cur.j] + cur.u * kBQB;
+    const int32_t r0 = row_of(cur);
     const bool more = t + 1 < total;
     StepPos nxt = cur;
     int32_t sn = si, rn = 0;
     if (more) {
       nxt = advance(cur);
       sn = sm.wseg[nxt.j];
-      rn = sm.wfirst[nxt.j] + nxt.u * kBQB;
+      rn = row_of(nxt);
       stage_load_a<D>(A, P, K, P.q[sn], hb_of(nxt), rn, tid, sa);
     }
     if constexpr (S_WAVE) {

@@ -39,12 +39,12 @@ __device__ inline void fwd_load_tile(const FwdArgs& A, const Plan& P, int b, int
     const int key = ch / (D / 8), dc = ch % (D / 8);
     kr[j] = ldg16(kb + key * D + dc * 8);
   }
-  const _Float16* vb = A.vt + (int64_t)(b * P.hkv + g) * D * P.nkc + c;
+  const _Float16* vb = A.vt + (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // [D][64] tile
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
     const int ch = tid + 256 * j;
     const int d = ch / (kBK / 8), kc = ch % (kBK / 8);
-    vr[j] = ldg16(vb + (int64_t)d * P.nkc + kc * 8);
+    vr[j] = ldg16(vb + d * kBK + kc * 8);
   }
 }
 

@@ -16,7 +16,8 @@ struct TensorArg {
 // ---------------------------------------------------------------- packing
 // Compact key space: the call's key segments back to back, each starting at
 // a multiple of kAlign, zero padded.  Natural layouts are [batch][hkv][nkc][d]
-// bf16; transposed ones [batch][hkv][d][nkc] fp16 with perm16 groups.
+// bf16; transposed ones fp16 [batch][hkv][nkc/64][d][64] (tiles of 64 rows,
+// each contiguous) with perm16 groups.
 struct PackKArgs {
   TensorArg k_clean, v_clean, k_corr, v_corr;  // bf16
   uint16_t* kn;   // natural K (nullable)
@@ -33,7 +34,7 @@ struct PackQArgs {
   const float* delta;  // [batch][R][hq]
   uint16_t* qn;        // [batch][hq][nqc][d] bf16
   uint16_t* don;
-  _Float16* qt;        // [batch][hq][d][nqc] fp16, perm16 groups of rows
+  _Float16* qt;        // [batch][hq][nqc/64][d][64] fp16 tiles, perm16 groups of rows
   _Float16* dot;
   float* lse2;         // [batch][hq][nqc] log2-scaled LSE; +inf on padding rows
   float* dc;           // [batch][hq][nqc] delta; 0 on padding rows

@@ -3,8 +3,10 @@
 //  pack_k: gathers the call's key rows (clean token ranges, then the share's
 //          packed corrupted rows) into one compact, zero-padded key space;
 //          writes natural bf16 K/V and fp16 K^T/V^T.  The transposed copies
-//          hold every aligned group of 16 keys in perm16 order, the order in
-//          which an MFMA C tile delivers its rows as a B operand.
+//          are tiled: each tile of 64 rows is one contiguous [d][64] block
+//          (so a consumer's tile is a single 16 KB read), and every aligned
+//          group of 16 rows is in perm16 order, the order in which an MFMA C
+//          tile delivers its rows as a B operand.
 //  pack_q: the same for the share's query side of the backward (Q, dO,
 //          natural and transposed), plus log2-scaled LSE and delta per row.
 //  delta:  D_i = sum_t dO_i[t] O_i[t], the softmax backward's row term.
@@ -18,7 +20,8 @@ namespace bd {
 
 namespace {
 
-constexpr int kPT = 64;  // rows per packing block
+constexpr int kPT = 64;  // rows per packing block = rows per transposed tile
+static_assert(kPT == kBK && kPT == kBQB, "transposed tiles are read whole by the kernels");
 
 template <int D>
 struct __attribute__((aligned(16))) PackSmem {
@@ -28,10 +31,10 @@ struct __attribute__((aligned(16))) PackSmem {
 
 __device__ inline _Float16 bf16_to_f16(uint16_t u) { return (_Float16)bf16_to_f32(u); }
 
-// Writes the transposed, perm16-ordered fp16 tile [D][kPT] from LDS rows.
+// Writes the transposed, perm16-ordered fp16 tile [D][kPT] (contiguous) from LDS rows.
 template <int D>
-__device__ inline void store_transposed(const uint16_t (*rows)[D + 8], _Float16* out, int64_t ld,
-                                        int tid) {
+__device__ inline void store_transposed(const uint16_t (*rows)[D + 8], _Float16* out, int tid) {
+  constexpr int ld = kPT;
   // each thread writes 8 consecutive slots (16 bytes) of one output row
   for (int ch = tid; ch < D * (kPT / 8); ch += 256) {
     const int d = ch / (kPT / 8), s0 = (ch % (kPT / 8)) * 8;
@@ -74,9 +77,9 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
     *reinterpret_cast<u32x4*>(&sm.b[r][dc]) = vv;
   }
   __syncthreads();
-  const int64_t tb = (int64_t)(b * P.hkv + g) * D * P.nkc + c;
-  if (A.kt) store_transposed<D>(sm.a, A.kt + tb, P.nkc, tid);
-  if (A.vt) store_transposed<D>(sm.b, A.vt + tb, P.nkc, tid);
+  const int64_t tb = (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // tile c / kPT
+  if (A.kt) store_transposed<D>(sm.a, A.kt + tb, tid);
+  if (A.vt) store_transposed<D>(sm.b, A.vt + tb, tid);
 }
 
 template <int D>
@@ -121,9 +124,9 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
     A.dc[hb * P.nqc + c + tid] = dd;
   }
   __syncthreads();
-  const int64_t tb = hb * D * P.nqc + c;
-  store_transposed<D>(sm.a, A.qt + tb, P.nqc, tid);
-  store_transposed<D>(sm.b, A.dot + tb, P.nqc, tid);
+  const int64_t tb = hb * D * P.nqc + (int64_t)c * D;  // tile c / kPT
+  store_transposed<D>(sm.a, A.qt + tb, tid);
+  store_transposed<D>(sm.b, A.dot + tb, tid);
 }
 
 // D_i = dO_i . O_i: 16 lanes per (batch, row, head), 8 elements per lane.
