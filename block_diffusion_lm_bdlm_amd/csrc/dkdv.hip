@@ -33,7 +33,9 @@ namespace bd {
 
 namespace {
 
-constexpr int kNB = kBQB / 32;  // 32-row MFMA blocks per step
+constexpr int kNB = kBQB / 32;     // 32-row MFMA blocks per step
+constexpr int kPairs = kBKB / 32;  // S-wave / P-wave pairs per workgroup, 32 keys each
+static_assert(kBQB % 32 == 0 && 64 % kBQB == 0, "steps are whole MFMA blocks inside one 64-row tile");
 
 template <int D>
 struct __attribute__((aligned(16))) DkdvSmem {
@@ -48,7 +50,7 @@ struct __attribute__((aligned(16))) DkdvSmem {
   int32_t vlo[2][kBQB];  // row sees key sources [vlo, vhi) of this key tile's segment
   int32_t vhi[2][kBQB];
   // P from each S-wave to its P-wave, in the MFMA C-tile order of each lane
-  _Float16 xchg[4][kNB][64][16];
+  _Float16 xchg[kPairs][kNB][64][16];
   // steps of the walk: segment s contributes wcount[s] steps from row wfirst[s]
   int32_t wseg[kMaxQSeg], wfirst[kMaxQSeg], wcount[kMaxQSeg];
   int32_t wn, wper;
@@ -60,20 +62,20 @@ struct StepPos {
   int32_t k, j, hs;
 };
 
-constexpr int kThreads = 512;  // 8 waves
+constexpr int kThreads = 128 * kPairs;  // two waves per pair
 
 // Prefetch of one step, in two halves so each is live for half a step:
 // A = natural Q, dO and the per-row data; B = transposed Q^T, dO^T.
 template <int D>
 struct StageA {
-  static constexpr int NCH = kBQB * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
+  static constexpr int NCH = (kBQB * D / 8 + kThreads - 1) / kThreads;  // 16-byte chunks per thread per tensor
   u32x4 r[2 * NCH];
   float l2, dd;
   int32_t lo, hi;
 };
 template <int D>
 struct StageB {
-  static constexpr int NCH = kBQB * D / 8 / kThreads;
+  static constexpr int NCH = (kBQB * D / 8 + kThreads - 1) / kThreads;
   u32x4 r[2 * NCH];
 };
 
@@ -85,6 +87,7 @@ __device__ inline void stage_load_a(const DkdvArgs& A, const Plan& P, const KSeg
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int ch = tid + kThreads * j;
+    if (ch >= kBQB * D / 8) break;
     const int row = ch / (D / 8), dcol = ch % (D / 8);
     st.r[j] = ldg16(A.qn + (hb * P.nqc + cq + row) * D + dcol * 8);
     st.r[NCH + j] = ldg16(A.don + (hb * P.nqc + cq + row) * D + dcol * 8);
@@ -115,8 +118,10 @@ __device__ inline void stage_load_b(const DkdvArgs& A, const Plan& P, const QSeg
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int ch = tid + kThreads * j;
+    if (ch >= kBQB * D / 8) break;
     const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
-    const int64_t t = hb * D * P.nqc + (int64_t)cq * D + d * kBQB + sc * 8;  // [D][64] tile of row cq
+    // row cq lies in the 64-row tile cq / 64, stored [D][64]
+    const int64_t t = hb * D * P.nqc + (int64_t)(cq & ~63) * D + d * 64 + (cq & 63) + sc * 8;
     st.r[j] = ldg16(A.qt + t);
     st.r[NCH + j] = ldg16(A.dot + t);
   }
@@ -128,6 +133,7 @@ __device__ inline void stage_store_a(DkdvSmem<D>& sm, int buf, int tid, const St
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int ch = tid + kThreads * j;
+    if (ch >= kBQB * D / 8) break;
     const int row = ch / (D / 8), dcol = ch % (D / 8);
     *reinterpret_cast<u32x4*>(&sm.q[buf][row * DkdvSmem<D>::NS + dcol * 8]) = st.r[j];
     *reinterpret_cast<u32x4*>(&sm.dO[buf][row * DkdvSmem<D>::NS + dcol * 8]) = st.r[NCH + j];
@@ -146,6 +152,7 @@ __device__ inline void stage_store_b(DkdvSmem<D>& sm, int buf, int tid, const St
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int ch = tid + kThreads * j;
+    if (ch >= kBQB * D / 8) break;
     const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
     *reinterpret_cast<u32x4*>(&sm.qt[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[j];
     *reinterpret_cast<u32x4*>(&sm.dot[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[NCH + j];
@@ -338,10 +345,10 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
 
 template <int D>
 __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int b, int g, int32_t ktile) {
-  static_assert(kBQB * D / 8 >= kThreads && (kBQB * D / 8) % kThreads == 0, "chunking");
+  static_assert(kThreads >= kBQB, "one thread per row stages the per-row data");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
-  const int kw = wave & 3;            // which 32 keys of the tile
-  const bool s_wave = wave < 4;       // S-wave (dV) or P-wave (dK)
+  const int kw = wave % kPairs;       // which 32 keys of the tile
+  const bool s_wave = wave < kPairs;  // S-wave (dV) or P-wave (dK)
   int32_t kseg, koff;
   ktile_locate(P, ktile, &kseg, &koff);
   const KSeg K = P.k[kseg];

@@ -21,7 +21,7 @@ namespace bd {
 namespace {
 
 constexpr int kPT = 64;  // rows per packing block = rows per transposed tile
-static_assert(kPT == kBK && kPT == kBQB, "transposed tiles are read whole by the kernels");
+static_assert(kPT == kBK && kPT % kBQB == 0, "kernels read whole transposed tiles or aligned parts");
 
 template <int D>
 struct __attribute__((aligned(16))) PackSmem {
