@@ -117,6 +117,118 @@ def cpu_baseline(work, q, k, v, do, nrows, seed=0):
                       f"useful FLOPs 8*d per visible pair; {dt:.1f} s"}
 
 
+def share_pairs(L, M, blocks, clean_q):
+    """Visible (query, key) pairs per head of a share over every key."""
+    blocks = np.asarray(blocks, dtype=np.int64)
+    n = int(((blocks + 1) * M).sum() * M)  # corrupted block b: M rows x (b+1)M keys
+    for lo, hi in clean_q:
+        t = np.arange(lo, hi, dtype=np.int64)
+        n += int(((t // M + 1) * M).sum())
+    return n
+
+
+def report_all(reps=3):
+    """Times every benchmark workload (stderr table, one JSON line per
+    workload on stdout).  Not the headline line: that is the default run."""
+    import torch
+
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd import synth
+    from block_diffusion_lm_bdlm_amd.runner import CsbpShare, WholeMask
+
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows = []
+    whole = [("fp32_L1K_M16_h4_d64_fwd", 0, (1, 1024, 16, 4, 4, 64), torch.float32, 1.0, False),
+             ("bf16_L8K_M32_b2_h16kv8", 1, (2, 8192, 32, 16, 8, 128), torch.bfloat16, 128 ** -0.5, True),
+             ("bf16_L64K_M32_h40kv8", 2, (1, 65536, 32, 40, 8, 128), torch.bfloat16, 1.0, True)]
+    for name, idx, (batch, L, M, hq, hkv, d), dt, std, bwd in whole:
+        seed = synth.SEED_BASE + idx
+        n2 = 2 * L
+        q = synth.normal((batch, n2, hq, d), seed, "q", dev, dt, std)
+        k = synth.normal((batch, n2, hkv, d), seed, "k", dev, dt, std)
+        v = synth.normal((batch, n2, hkv, d), seed, "v", dev, dt, std)
+        do = synth.normal((batch, n2, hq, d), seed, "do", dev, torch.bfloat16)
+        wm = WholeMask(batch, L, M, hq, hkv, d, B.BDATTN_F32 if dt == torch.float32 else B.BDATTN_BF16)
+        wf, wb = wm.workspace(False, dev), wm.workspace(True, dev)
+        grads = wm.alloc_grads(dev)
+        state = {}
+
+        def fwd():
+            state["o"], state["lse"] = wm.fwd(q, k, v, ws=wf)
+
+        def step():
+            fwd()
+            if bwd:
+                for g_ in grads[:5]:
+                    g_.zero_()
+                wm.bwd(q, k, v, state["o"], state["lse"], do, ws=wb, grads=grads)
+
+        ms = timed(step)
+        pairs = visible_pairs(L, M) * hq * batch
+        flops = (14 if bwd else 4) * d * pairs
+        rows.append((name, ms, flops, batch * L))
+        del q, k, v, do, wm, wf, wb, grads, state
+        torch.cuda.empty_cache()
+    shares = [("csbp_L256K_P8_r0_h32kv8", 3, 262144, 32, 32, 8, 8, False, 0.0),
+              ("csbp_L512K_P16_r0_h32kv4_outliers", 4, 524288, 16, 32, 4, 16, True, 0.01)]
+    for name, idx, L, M, hq, hkv, P, clean_queries, outl in shares:
+        d = 128
+        blocks = B.bdattn_assign_blocks(L // M, P, 0).tolist()
+        cs = B.bdattn_clean_shard(L, P, 0)
+        clean_q = [(cs.lo[0], cs.hi[0]), (cs.lo[1], cs.hi[1])] if clean_queries else []
+        shards = []
+        for s_ in range(P):
+            kk = B.bdattn_clean_shard(L, P, s_)
+            shards.append([(kk.lo[0], kk.hi[0]), (kk.lo[1], kk.hi[1])])
+        seed = synth.SEED_BASE + idx
+        n_clean = sum(hi - lo for lo, hi in clean_q)
+        nx = len(blocks) * M
+        f = dict(device=dev, outlier_frac=outl)
+        qc = synth.normal((1, max(n_clean, 1), hq, d), seed, "q_clean", **f)[:, :n_clean]
+        qx = synth.normal((1, nx, hq, d), seed, "q_corr", **f)
+        kx = synth.normal((1, nx, hkv, d), seed, "k_corr", **f)
+        vx = synth.normal((1, nx, hkv, d), seed, "v_corr", **f)
+        kc = synth.normal((1, L, hkv, d), seed, "k", **f)
+        vc = synth.normal((1, L, hkv, d), seed, "v", **f)
+        sh = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, shards)
+        do = synth.normal((1, sh.R, hq, d), seed, "do", dev)
+        wf, wb = sh.workspace(False, dev), sh.workspace(True, dev)
+        grads = sh.alloc_grads(dev)
+
+        def step():
+            o32, lse, _ = sh.fwd(qc, qx, kc, vc, kx, vx, ws=wf)
+            for g_ in grads[:5]:
+                g_.zero_()
+            sh.bwd(qc, qx, kc, vc, kx, vx, o32, lse, do, ws=wb, grads=grads)
+
+        ms = timed(step)
+        flops = 14 * d * share_pairs(L, M, blocks, clean_q) * hq
+        rows.append((name, ms, flops, L // P))
+        del qc, qx, kx, vx, kc, vc, sh, do, wf, wb, grads
+        torch.cuda.empty_cache()
+    print(f"{'workload':36s} {'ms':>9s} {'useful TF/s':>12s} {'% of 2.5PF':>10s} {'tokens/s':>12s}",
+          file=sys.stderr)
+    for name, ms, flops, toks in rows:
+        tf = flops / (ms * 1e-3) / 1e12
+        print(f"{name:36s} {ms:9.2f} {tf:12.1f} {100 * tf / PEAK_BF16_TFLOPS:10.2f} {toks / (ms * 1e-3):12.0f}",
+              file=sys.stderr)
+        print(json.dumps({"workload": name, "ms": round(ms, 3), "useful_tflops": round(tf, 2),
+                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "tokens_per_s": round(toks / (ms * 1e-3), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,9 +238,14 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--report-all", action="store_true",
+                    help="time every benchmark workload (table on stderr) and exit")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.report_all:
+        report_all()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the hot path; runs on more than one GPU are not "

@@ -111,3 +111,23 @@ def test_deterministic_grads(dev):
     b = wm.bwd(q, k, v, o, lse, do)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# Block sizes of the pages' robustness ablation (128 to 1,024 tokens per
+# block; wiki note, "Key numbers") and the token-causal clean copy, at
+# shapes the full oracle still covers.
+@pytest.mark.parametrize("shape", [(1, 2048, 1024, 2, 1, 128, False), (1, 1536, 512, 2, 2, 128, False),
+                                   (1, 1024, 256, 4, 2, 64, False), (1, 768, 128, 2, 1, 128, True)],
+                         ids=["M1024", "M512", "M256", "M128-token-causal"])
+def test_large_blocks(dev, orc, shape):
+    batch, L, M, hq, hkv, d, tc = shape
+    (q, k, v, do), got = _run(dev, shape, torch.bfloat16, seed=3)
+    p = orc.problem(batch, L, M, hq, hkv, d, token_causal=tc, bf16=True)
+    hq_, hk_, hv_, hdo = (host_bits(x) for x in (q, k, v, do))
+    o, lse = orc.fwd(p, orc.keys(), hq_, hk_, hv_)
+    assert max_abs(got["o"], o) <= TOL_O
+    assert max_abs(got["lse"], lse) <= TOL_LSE
+    dq, dk, dv = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), hq_, hk_, hv_, hdo)
+    assert rel_l2(got["dq"], dq) <= TOL_GRAD
+    assert rel_l2(got["dk"], dk) <= TOL_GRAD
+    assert rel_l2(got["dv"], dv) <= TOL_GRAD
