@@ -15,6 +15,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["bdattn.cpp", "fwd.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
+# Per-file code generation options.  dkdv.hip keeps its long-lived
+# accumulators in AGPRs (inline-assembly products) and asks for every other
+# matrix product in the VGPR form, so the scores feeding vector code need no
+# AGPR -> VGPR copies.  Its global->LDS copies set M0 in inline assembly; the
+# file makes no other use of M0, so the reserved-register warning is off.
+EXTRA = {"dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]}
 ARCH = os.environ.get("BDATTN_ARCH", "gfx950")
 
 
@@ -34,7 +40,7 @@ def _flags():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + _flags()
+    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + _flags() + EXTRA.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

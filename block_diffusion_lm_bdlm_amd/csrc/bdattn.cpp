@@ -167,6 +167,7 @@ struct BwdWs {
   uint16_t *qn, *don;
   _Float16 *qt, *dot;
   float *lse2, *dc;
+  int32_t* vis;
 };
 
 size_t carve_fwd(const Plan& P, bool f32, char* base, FwdWs* w) {
@@ -195,6 +196,7 @@ size_t carve_bwd(const Plan& P, char* base, BwdWs* w) {
   t.dot = cv.take<_Float16>(nq);
   t.lse2 = cv.take<float>(nr);
   t.dc = cv.take<float>(nr);
+  t.vis = cv.take<int32_t>((size_t)4 * P.nqc);
   if (w) *w = t;
   return cv.off;
 }
@@ -437,7 +439,7 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
     if (e != hipSuccess) return BDATTN_EHIP;
   }
   PackQArgs pq{targ(q_clean), targ(q_corr), targ(d_o), lse_final, delta, ws.qn, ws.don, ws.qt, ws.dot,
-               ws.lse2, ws.dc};
+               ws.lse2, ws.dc, ws.vis};
   e = timed(K_PACK_Q, s, [&] { return launch_pack_q(P, pq, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   if (P.nkc == 0) return BDATTN_OK;  // no key in this call: nothing to add
@@ -452,7 +454,7 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   pk.kt = ws.kt;
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DkdvArgs ka{ws.qn, ws.don, ws.qt, ws.dot, ws.lse2, ws.dc, ws.kn, ws.vn,
+  DkdvArgs ka{ws.qn, ws.don, ws.qt, ws.dot, ws.lse2, ws.dc, ws.vis, ws.kn, ws.vn,
               dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc};
   e = timed(K_DKDV, s, [&] { return launch_dkdv(P, ka, s); });
   if (e != hipSuccess) return BDATTN_EHIP;

@@ -9,22 +9,27 @@
 //
 // A workgroup owns 128 keys of one KV head and runs 8 waves, two per SIMD,
 // in pairs that own the same 32 keys:
-//   S-wave: K in registers; S = Q K^T, P = exp(S - LSE) (masked), writes P
-//           to LDS, accumulates dV^T += dO^T P.
+//   S-wave: K in registers; S = Q K^T, P = exp(S - LSE) (masked), hands P
+//           to its partner through LDS, accumulates dV^T += dO^T P.
 //   P-wave: V in registers; dP = dO V^T, reads P, dS = P (dP - D),
 //           accumulates dK^T += Q^T dS.
 // Each key has exactly one writer per gradient, so no atomics are needed,
 // and the two waves of a SIMD overlap one's vector work with the other's
-// matrix work.  The workgroup walks every query row (of every query head of
-// the group) that sees its keys, in steps of 64 rows staged through LDS
-// (natural Q, dO for S and dP; transposed fp16 Q^T, dO^T for the
-// contractions over rows).
+// matrix work.  (The keys per wave are a parameter: 64 keys per wave make
+// each LDS fragment feed two products but need one wave per SIMD, which
+// measured slower.)
+// The workgroup walks every query row (of every query head of the group)
+// that sees its keys, in steps of 64 rows.  Each step's operands (natural Q,
+// dO for S and dP; transposed fp16 Q^T, dO^T for the contractions over rows;
+// per-row log2 LSE, D and visible key interval) go from global memory
+// straight into LDS through the load units (global_load_lds), double
+// buffered, into unpadded tiles whose 16-byte chunks are XOR-swizzled by
+// row, so the fragment reads are free of bank conflicts; the step after
+// next is touched into L2 meanwhile.
 // The walk runs back to front by position (all heads of the group at each
 // position): the last rows are seen by every key tile, so the workgroups
-// resident on one XCD stay on the same rows and share them through L2.  Each step stages per-row visibility bounds next to LSE and D,
-// so a step that straddles the mask boundary needs no division per element.
+// resident on one XCD stay on the same rows and share them through L2.
 #include <climits>
-#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -33,28 +38,328 @@ namespace bd {
 
 namespace {
 
-constexpr int kNB = kBQB / 32;     // 32-row MFMA blocks per step
-constexpr int kPairs = kBKB / 32;  // S-wave / P-wave pairs per workgroup, 32 keys each
-static_assert(kBQB % 32 == 0 && 64 % kBQB == 0, "steps are whole MFMA blocks inside one 64-row tile");
+constexpr int kKW = 32;               // keys per wave
+constexpr int kPairs = kBKB / kKW;    // S-wave / P-wave pairs per workgroup
+constexpr int kWaves = 2 * kPairs;    // two waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRB = kBQB / 32;        // 32-row MFMA blocks per step
+constexpr int kKB = kKW / 32;         // 32-key MFMA blocks per wave
+static_assert(kBKB % kKW == 0 && kKW % 32 == 0, "whole 32-key blocks per wave");
+static_assert(kBQB == 64, "one lane per row stages the per-row data; 64-row transposed tiles");
+static_assert(kWaves >= 4, "the four per-row arrays are staged one per wave");
 
+typedef __attribute__((address_space(3))) const void lds_void;
+
+// Copies 16 (4) bytes per lane from global memory at sbase + voff into LDS
+// at `lds` + 16 lane (4 lane); sbase and lds are the same for the whole wave.
+// Written as inline assembly so the compiler does not order the copy
+// against unrelated LDS reads; completion is awaited explicitly
+// (wait_copies) before the barrier that publishes the data.  M0 (the LDS
+// address) needs one wait state before the copy reads it.
+__device__ __forceinline__ void copy16(const void* sbase, uint32_t voff, const void* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(la)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4(const void* sbase, uint32_t voff, const void* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(la)
+               : "memory", "m0");
+}
+// Marks a value that is the same in every lane as such (scalar registers).
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)x);
+  const int32_t hi = __builtin_amdgcn_readfirstlane((int32_t)(x >> 32));
+  return ((int64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// Waits for all but the N most recent copies (vector memory operations
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_copies_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+
+// Barrier that orders this wave's LDS writes before its partners' reads,
+// without waiting for the copies still in flight.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Staged tiles are unpadded; 16-byte chunk c of row r sits at chunk
+// position c ^ swz(r).  The LDS serves a 128-bit read 16 lanes (256 bytes)
+// at a time, so the 16 rows one fragment read touches must land on 16
+// different 16-byte bank groups: swz(r) = r & 15 for 256-byte rows and
+// (r >> 1) & 7 for 128-byte rows (two rows share a 256-byte bank line).
 template <int D>
 struct __attribute__((aligned(16))) DkdvSmem {
-  static constexpr int NS = D + 8;     // natural row stride (bf16)
-  static constexpr int TS = kBQB + 8;  // transposed row stride (fp16)
-  uint16_t q[2][kBQB * NS];
-  uint16_t dO[2][kBQB * NS];
-  _Float16 qt[2][D * TS];
-  _Float16 dot[2][D * TS];
+  static constexpr int TILE = kBQB * D;  // elements per staged tile
+  uint16_t q[2][TILE];                   // natural bf16 [row][d]
+  uint16_t dO[2][TILE];
+  _Float16 qt[2][TILE];                  // transposed fp16 [d][row], perm16 rows
+  _Float16 dot[2][TILE];
   float lse2[2][kBQB];
   float dc[2][kBQB];
-  int32_t vlo[2][kBQB];  // row sees key sources [vlo, vhi) of this key tile's segment
+  int32_t vlo[2][kBQB];  // row sees key sources [vlo, vhi) of the tile's kind
   int32_t vhi[2][kBQB];
   // P from each S-wave to its P-wave, in the MFMA C-tile order of each lane
-  _Float16 xchg[kPairs][kNB][64][16];
+  _Float16 xchg[kPairs][kRB][kKB][2][64][8];
+  float touch[kWaves][64];  // landing slot of the L2 prefetches (never read)
   // steps of the walk: segment s contributes wcount[s] steps from row wfirst[s]
   int32_t wseg[kMaxQSeg], wfirst[kMaxQSeg], wcount[kMaxQSeg];
   int32_t wn, wper;
 };
+
+template <int NC>  // chunks per row: 16 (256-byte rows) or 8 (128-byte rows)
+__host__ __device__ constexpr int swz(int r) {
+  static_assert(NC == 16 || NC == 8, "rows of 128 or 256 bytes");
+  return NC == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Per-lane element offsets into the swizzled tiles.  A fragment read takes
+// logical chunk 2 k + hh (k-th 16-element step, lane half hh) of row
+// 32 m + ql; swz(32 m + ql) = swz(ql).
+template <int D>
+struct LaneOff {
+  int nat[D / 16];     // natural rows (D / 8 chunks)
+  int tr[kBQB / 16];   // transposed rows (8 chunks)
+  uint32_t dn, dt;     // byte offsets of this lane's first copied chunk (natural, transposed)
+};
+
+template <int D>
+__device__ inline LaneOff<D> lane_offsets(int wave, int lane) {
+  constexpr int NCR = D / 8;  // chunks per natural row
+  static_assert((kWaves * 64 / NCR) % 16 == 0 && (kWaves * 8) % 16 == 0,
+                "a wave's later copy blocks keep its rows' swizzle");
+  const int ql = lane & 31, hh = lane >> 5;
+  LaneOff<D> o;
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) o.nat[k] = ((2 * k + hh) ^ swz<NCR>(ql)) * 8;
+#pragma unroll
+  for (int k = 0; k < kBQB / 16; ++k) o.tr[k] = ((2 * k + hh) ^ swz<8>(ql)) * 8;
+  const int p = wave * 64 + lane;  // physical chunk of the wave's first 1 KB block
+  const int row = p / NCR;
+  o.dn = (uint32_t)(row * D + ((p % NCR) ^ swz<NCR>(row)) * 8) * 2;
+  const int d = p / 8;
+  o.dt = (uint32_t)(d * kBQB + ((p % 8) ^ swz<8>(d)) * 8) * 2;
+  return o;
+}
+
+// acc += A B with the accumulator held in AGPRs for the whole walk.  The
+// product is written as inline assembly so the accumulator stays in the
+// AGPRs while every other product (compiled in the VGPR form) feeds vector
+// code directly.  Inputs come from LDS reads and vector instructions, whose
+// results the hardware interlocks for the matrix core; the accumulator is
+// read back only after agpr_settle().
+__device__ __forceinline__ void mfma_f16_agpr(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states before vector code may read an accumulator that a product
+// just wrote (more than a 32x32x16 product's 16 passes).
+__device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
+// Fragment reads kept in flight ahead of the products that consume them;
+// scheduling barriers pin this order (the compiler otherwise sinks each
+// read to its first use).
+constexpr int kAhead = 6;
+
+// Issues the copies of one step (64 rows from compact row cq of head hb)
+// into buffer B.  Every wave copies its share of each tile.
+template <int D>
+__device__ __forceinline__ void stage(const DkdvArgs& A, const Plan& P, int kkind, int64_t hb, int64_t cq,
+                                      int wave, int lane, const LaneOff<D>& o, DkdvSmem<D>& sm, int B) {
+  constexpr int PER = kBQB * D / 512 / kWaves;  // 1 KB blocks per wave per tile
+  const int64_t base = uniform64((hb * P.nqc + cq) * D);  // natural and transposed tiles alike
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int blk = (wave + kWaves * j) * 512;  // elements
+    const int64_t e = base + (int64_t)j * kWaves * 512;
+    copy16(A.qn + e, o.dn, &sm.q[B][blk]);
+    copy16(A.don + e, o.dn, &sm.dO[B][blk]);
+    copy16(A.qt + e, o.dt, &sm.qt[B][blk]);
+    copy16(A.dot + e, o.dt, &sm.dot[B][blk]);
+  }
+  const uint32_t lo = (uint32_t)lane * 4;
+  switch (wave) {
+    case 0: copy4(A.lse2 + hb * P.nqc + cq, lo, &sm.lse2[B][0]); break;
+    case 1: copy4(A.dc + hb * P.nqc + cq, lo, &sm.dc[B][0]); break;
+    case 2: copy4(A.vis + (int64_t)(2 * kkind) * P.nqc + cq, lo, &sm.vlo[B][0]); break;
+    case 3: copy4(A.vis + (int64_t)(2 * kkind + 1) * P.nqc + cq, lo, &sm.vhi[B][0]); break;
+    default: break;
+  }
+}
+
+// Touches every 128-byte line of a step's four tiles so that they are in
+// L2 when their copies are issued one step later; the 4 bytes per lane land
+// in a scratch slot of LDS.  Touch i covers 64 lines of tile i / (D / 64);
+// wave w issues touches w, w + kWaves, ...
+template <int D>
+constexpr int kTouchTotal = 4 * D / 64;
+__device__ __forceinline__ int touches_of(int total, int wave) {
+  return wave < total ? (total - wave + kWaves - 1) / kWaves : 0;
+}
+
+template <int D>
+__device__ __forceinline__ void touch_l2(const DkdvArgs& A, const Plan& P, int64_t hb, int64_t cq, int wave,
+                                         int lane, DkdvSmem<D>& sm) {
+  constexpr int PT = D / 64;  // touches per tile
+  const int64_t base = uniform64((hb * P.nqc + cq) * D);
+#pragma unroll
+  for (int i0 = 0; i0 < kTouchTotal<D>; i0 += kWaves) {
+    const int i = i0 + wave;
+    if (i >= kTouchTotal<D>) break;
+    const uint32_t off = (uint32_t)((i % PT) * 64 + lane) * 128;
+    switch (i / PT) {
+      case 0: copy4(A.qn + base, off, &sm.touch[wave][0]); break;
+      case 1: copy4(A.don + base, off, &sm.touch[wave][0]); break;
+      case 2: copy4(A.qt + base, off, &sm.touch[wave][0]); break;
+      default: copy4(A.dot + base, off, &sm.touch[wave][0]); break;
+    }
+  }
+}
+
+// Waits until only this wave's `n` most recent copies (its touches) are
+// still in flight.
+__device__ __forceinline__ void wait_all_but(int n) {
+  if (n >= 2)
+    wait_copies_but<2>();
+  else if (n == 1)
+    wait_copies_but<1>();
+  else
+    wait_copies();
+}
+
+// S-wave, first half of a step: S = Q K^T, then P = exp2(S c2 - LSE2) on
+// visible pairs (every pair when FULL), in fp16, as the B operands of the
+// contraction over rows.
+template <int D, bool FULL>
+__device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int lane, int ql, int hh,
+                                          const int32_t (&mysrc)[kKB], float c2, const bf16x8 (&kreg)[kKB][D / 16],
+                                          const LaneOff<D>& o, f16x8 (&pf)[kRB][kKB][2]) {
+  constexpr int NKS = D / 16;
+  const uint16_t* qb = &sm.q[B][ql * D];
+  f32x16 sacc[kRB][kKB];
+  // fragment f = (rb, ks); kAhead reads stay in flight ahead of the products
+  constexpr int NF = kRB * NKS;
+  bf16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(qb + (f / NKS) * 32 * D + o.nat[f % NKS]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) {
+      const int g = f + kAhead;
+      fr[g] = ld16<bf16x8>(qb + (g / NKS) * 32 * D + o.nat[g % NKS]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+      sacc[f / NKS][kb] = mfma_bf16(fr[f], kreg[kb][f % NKS], f % NKS ? sacc[f / NKS][kb] : f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int r = rb * 32 + i4 * 8 + hh * 4;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[B][r]);
+      int32_t los[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, his[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+      if constexpr (!FULL) {
+        const int4 lo4 = *reinterpret_cast<const int4*>(&sm.vlo[B][r]);
+        const int4 hi4 = *reinterpret_cast<const int4*>(&sm.vhi[B][r]);
+        los[0] = lo4.x; los[1] = lo4.y; los[2] = lo4.z; los[3] = lo4.w;
+        his[0] = hi4.x; his[1] = hi4.y; his[2] = hi4.z; his[3] = hi4.w;
+      }
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i4 * 4 + e;
+          float x = fmaf(sacc[rb][kb][i], c2, -l4[e]);
+          if constexpr (!FULL) x = (mysrc[kb] >= los[e] && mysrc[kb] < his[e]) ? x : -INFINITY;
+          pf[rb][kb][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(x);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) *reinterpret_cast<f16x8*>(&sm.xchg[kw][rb][kb][ss][lane][0]) = pf[rb][kb][ss];
+  }
+}
+
+// Contraction over the step's rows: acc^T[d][key] += T^T[d][row] X[row][key]
+// with T^T a transposed tile and X (P or dS) in registers.
+template <int D>
+__device__ __forceinline__ void rows_contract(const _Float16* tile, int ql, const LaneOff<D>& o,
+                                              const f16x8 (&x)[kRB][kKB][2], f32x16 (&acc)[D / 32][kKB]) {
+  const _Float16* tb = tile + ql * kBQB;
+  // fragment f = (s, db); kAhead reads stay in flight ahead of the products
+  constexpr int NDB = D / 32, NF = (kBQB / 16) * NDB;
+  f16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBQB + o.tr[f / NDB]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) {
+      const int g = f + kAhead;
+      fr[g] = ld16<f16x8>(tb + (g % NDB) * 32 * kBQB + o.tr[g / NDB]);
+    }
+    const int s = f / NDB, db = f % NDB;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) mfma_f16_agpr(acc[db][kb], fr[f], x[s >> 1][kb][s & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// P-wave, first half of a step: dP = dO V^T.
+template <int D>
+__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const bf16x8 (&vreg)[kKB][D / 16],
+                                          const LaneOff<D>& o, f32x16 (&pacc)[kRB][kKB]) {
+  const uint16_t* ob = &sm.dO[B][ql * D];
+  constexpr int NKS = D / 16, NF = kRB * NKS;
+  bf16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(ob + (f / NKS) * 32 * D + o.nat[f % NKS]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) {
+      const int g = f + kAhead;
+      fr[g] = ld16<bf16x8>(ob + (g / NKS) * 32 * D + o.nat[g % NKS]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+      pacc[f / NKS][kb] = mfma_bf16(fr[f], vreg[kb][f % NKS], f % NKS ? pacc[f / NKS][kb] : f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// P-wave, second half: dS = P (dP - D) with P from its S-wave.
+template <int D>
+__device__ __forceinline__ void p_phase_ds(DkdvSmem<D>& sm, int B, int kw, int lane, int hh,
+                                           const f32x16 (&pacc)[kRB][kKB], f16x8 (&dsf)[kRB][kKB][2]) {
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dc[B][rb * 32 + (2 * ss) * 8 + hh * 4]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dc[B][rb * 32 + (2 * ss + 1) * 8 + hh * 4]);
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        const f16x8 p = ld16<f16x8>(&sm.xchg[kw][rb][kb][ss][lane][0]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dd = e < 4 ? d0[e & 3] : d1[e & 3];
+          dsf[rb][kb][ss][e] = (_Float16)((float)p[e] * (pacc[rb][kb][ss * 8 + e] - dd));
+        }
+      }
+    }
+}
 
 // Position of the walk: k-th step from the end of walk segment j, query head
 // hs within the group.
@@ -62,220 +367,14 @@ struct StepPos {
   int32_t k, j, hs;
 };
 
-constexpr int kThreads = 128 * kPairs;  // two waves per pair
-
-// Prefetch of one step, in two halves so each is live for half a step:
-// A = natural Q, dO and the per-row data; B = transposed Q^T, dO^T.
-template <int D>
-struct StageA {
-  static constexpr int NCH = (kBQB * D / 8 + kThreads - 1) / kThreads;  // 16-byte chunks per thread per tensor
-  u32x4 r[2 * NCH];
-  float l2, dd;
-  int32_t lo, hi;
-};
-template <int D>
-struct StageB {
-  static constexpr int NCH = (kBQB * D / 8 + kThreads - 1) / kThreads;
-  u32x4 r[2 * NCH];
-};
-
-template <int D>
-__device__ inline void stage_load_a(const DkdvArgs& A, const Plan& P, const KSeg& K, const QSeg& S, int64_t hb,
-                                    int32_t r0, int tid, StageA<D>& st) {
-  constexpr int NCH = StageA<D>::NCH;
-  const int32_t cq = S.tile0 * kBQ + r0;  // compact row of the step's first row
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int ch = tid + kThreads * j;
-    if (ch >= kBQB * D / 8) break;
-    const int row = ch / (D / 8), dcol = ch % (D / 8);
-    st.r[j] = ldg16(A.qn + (hb * P.nqc + cq + row) * D + dcol * 8);
-    st.r[NCH + j] = ldg16(A.don + (hb * P.nqc + cq + row) * D + dcol * 8);
-  }
-  if (tid < kBQB) {
-    st.l2 = A.lse2[hb * P.nqc + cq + tid];
-    st.dd = A.dc[hb * P.nqc + cq + tid];
-    const int32_t rr = r0 + tid;
-    st.lo = 0;
-    st.hi = 0;
-    if (rr < S.nrows) {
-      const RowBounds rb = row_bounds(P, S, rr);
-      if (K.kind == KIND_CLEAN) {
-        st.hi = rb.hi_clean;
-      } else if (S.kind == KIND_CORR) {
-        st.lo = rb.lo_loc;
-        st.hi = rb.hi_loc;
-      }
-    }
-  }
-}
-
-template <int D>
-__device__ inline void stage_load_b(const DkdvArgs& A, const Plan& P, const QSeg& S, int64_t hb, int32_t r0,
-                                    int tid, StageB<D>& st) {
-  constexpr int NCH = StageB<D>::NCH;
-  const int32_t cq = S.tile0 * kBQ + r0;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int ch = tid + kThreads * j;
-    if (ch >= kBQB * D / 8) break;
-    const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
-    // row cq lies in the 64-row tile cq / 64, stored [D][64]
-    const int64_t t = hb * D * P.nqc + (int64_t)(cq & ~63) * D + d * 64 + (cq & 63) + sc * 8;
-    st.r[j] = ldg16(A.qt + t);
-    st.r[NCH + j] = ldg16(A.dot + t);
-  }
-}
-
-template <int D>
-__device__ inline void stage_store_a(DkdvSmem<D>& sm, int buf, int tid, const StageA<D>& st) {
-  constexpr int NCH = StageA<D>::NCH;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int ch = tid + kThreads * j;
-    if (ch >= kBQB * D / 8) break;
-    const int row = ch / (D / 8), dcol = ch % (D / 8);
-    *reinterpret_cast<u32x4*>(&sm.q[buf][row * DkdvSmem<D>::NS + dcol * 8]) = st.r[j];
-    *reinterpret_cast<u32x4*>(&sm.dO[buf][row * DkdvSmem<D>::NS + dcol * 8]) = st.r[NCH + j];
-  }
-  if (tid < kBQB) {
-    sm.lse2[buf][tid] = st.l2;
-    sm.dc[buf][tid] = st.dd;
-    sm.vlo[buf][tid] = st.lo;
-    sm.vhi[buf][tid] = st.hi;
-  }
-}
-
-template <int D>
-__device__ inline void stage_store_b(DkdvSmem<D>& sm, int buf, int tid, const StageB<D>& st) {
-  constexpr int NCH = StageB<D>::NCH;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int ch = tid + kThreads * j;
-    if (ch >= kBQB * D / 8) break;
-    const int d = ch / (kBQB / 8), sc = ch % (kBQB / 8);
-    *reinterpret_cast<u32x4*>(&sm.qt[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[j];
-    *reinterpret_cast<u32x4*>(&sm.dot[buf][d * DkdvSmem<D>::TS + sc * 8]) = st.r[NCH + j];
-  }
-}
-
-// S-wave, one 32-row block: P = exp2(S c2 - LSE2) on visible pairs, in fp16,
-// packed as the two B operands (k-steps) of the contraction over rows.
-__device__ __forceinline__ void block_p(bool full, const f32x16& sacc, const float* lse2, const int32_t* vlo,
-                                        const int32_t* vhi, int hh, int32_t mysrc, float c2,
-                                        f16x8 (&pf)[2]) {
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const int rb = i4 * 8 + hh * 4;  // C rows rb .. rb+3 of the block
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + rb);
-    // full steps: every row sees every key, [INT_MIN, INT_MAX) admits all
-    int4 lo4 = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, hi4 = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-    if (!full) {
-      lo4 = *reinterpret_cast<const int4*>(vlo + rb);
-      hi4 = *reinterpret_cast<const int4*>(vhi + rb);
-    }
-    const int32_t los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-    const int32_t his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = i4 * 4 + e;
-      const float x = (mysrc >= los[e] && mysrc < his[e]) ? fmaf(sacc[i], c2, -l4[e]) : -INFINITY;
-      pf[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(x);
-    }
-  }
-}
-
-// S-wave, first half of a step: S = Q K^T and P (kept in pf, copied to LDS).
-template <int D>
-__device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, bool full, int BUF, int kw, int lane, int ql, int hh,
-                                          int32_t mysrc, float c2, const bf16x8 (&kreg)[D / 16],
-                                          f16x8 (&pf)[kNB][2]) {
-  constexpr int NS = DkdvSmem<D>::NS;
-  const uint16_t* qb = &sm.q[BUF][ql * NS + hh * 8];
-  f32x16 sacc[kNB];
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) sacc[blk] = f32x16{};
-  // consecutive products feed different accumulators (independent chains)
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-    for (int blk = 0; blk < kNB; ++blk)
-      sacc[blk] = mfma_bf16(ld16<bf16x8>(qb + blk * 32 * NS + ks * 16), kreg[ks], sacc[blk]);
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) {
-    block_p(full, sacc[blk], &sm.lse2[BUF][blk * 32], &sm.vlo[BUF][blk * 32], &sm.vhi[BUF][blk * 32], hh,
-            mysrc, c2, pf[blk]);
-    *reinterpret_cast<f16x8*>(&sm.xchg[kw][blk][lane][0]) = pf[blk][0];
-    *reinterpret_cast<f16x8*>(&sm.xchg[kw][blk][lane][8]) = pf[blk][1];
-  }
-}
-
-// S-wave, second half: dV^T += dO^T P.
-template <int D>
-__device__ __forceinline__ void s_phase_b(DkdvSmem<D>& sm, int BUF, int ql, int hh, const f16x8 (&pf)[kNB][2],
-                                          f32x16 (&dvacc)[D / 32]) {
-  constexpr int TS = DkdvSmem<D>::TS;
-  const _Float16* otb = &sm.dot[BUF][ql * TS + hh * 8];
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk)
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dvacc[db] = mfma_f16(ld16<f16x8>(otb + db * 32 * TS + blk * 32 + ss * 16), pf[blk][ss], dvacc[db]);
-}
-
-// P-wave, first half of a step: dP = dO V^T.
-template <int D>
-__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int BUF, int ql, int hh, const bf16x8 (&vreg)[D / 16],
-                                          f32x16 (&pacc)[kNB]) {
-  constexpr int NS = DkdvSmem<D>::NS;
-  const uint16_t* ob = &sm.dO[BUF][ql * NS + hh * 8];
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) pacc[blk] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-    for (int blk = 0; blk < kNB; ++blk)
-      pacc[blk] = mfma_bf16(ld16<bf16x8>(ob + blk * 32 * NS + ks * 16), vreg[ks], pacc[blk]);
-}
-
-// P-wave, second half: dS = P (dP - D) with P from its S-wave, dK^T += Q^T dS.
-template <int D>
-__device__ __forceinline__ void p_phase_b(DkdvSmem<D>& sm, int BUF, int kw, int lane, int ql, int hh,
-                                          const f32x16 (&pacc)[kNB], f32x16 (&dkacc)[D / 32]) {
-  constexpr int TS = DkdvSmem<D>::TS;
-  const _Float16* qtb = &sm.qt[BUF][ql * TS + hh * 8];
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) {
-    const f16x8 p0 = ld16<f16x8>(&sm.xchg[kw][blk][lane][0]);
-    const f16x8 p1 = ld16<f16x8>(&sm.xchg[kw][blk][lane][8]);
-    f16x8 dsf[2];
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dc[BUF][blk * 32 + i4 * 8 + hh * 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i4 * 4 + e;
-        const float p = (float)((i < 8) ? p0[i & 7] : p1[i & 7]);
-        dsf[i >> 3][i & 7] = (_Float16)(p * (pacc[blk][i] - d4[e]));
-      }
-    }
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dkacc[db] = mfma_f16(ld16<f16x8>(qtb + db * 32 * TS + blk * 32 + ss * 16), dsf[ss], dkacc[db]);
-  }
-}
-
 // The query walk of one role.  S-waves and P-waves run the same sequence of
-// barriers: two per step (after P is exchanged, after the prefetch lands).
+// barriers: two per step (after P is exchanged, after the next step lands).
 template <int D, bool S_WAVE>
 __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, const KSeg& K, int b,
-                                          int g, int32_t kvalid, int32_t kt1, int tid, int kw, int lane, int ql,
-                                          int hh, int32_t mysrc, int32_t nseg, int32_t total,
-                                          const bf16x8 (&kvreg)[D / 16], f32x16 (&acc)[D / 32]) {
+                                          int g, int32_t kvalid, int32_t kt1, int wave, int kw, int lane, int ql,
+                                          int hh, const int32_t (&mysrc)[kKB], int32_t nseg, int32_t total,
+                                          const LaneOff<D>& o, const bf16x8 (&kvreg)[kKB][D / 16],
+                                          f32x16 (&acc)[D / 32][kKB]) {
   const float c2 = P.scale_log2;
   // Walk back to front by position: the k-th step from the end of every
   // segment, for every query head, then step k+1.  Every key tile's rows
@@ -290,65 +389,120 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
         p.j = nseg - 1;
         ++p.k;
       }
-    } while (p.k >= sm.wcount[p.j]);
+    } while (p.k >= uniform(sm.wcount[p.j]));
     return p;
   };
-  auto row_of = [&](const StepPos& p) { return sm.wfirst[p.j] + (sm.wcount[p.j] - 1 - p.k) * kBQB; };
+  auto row_of = [&](const StepPos& p) {
+    return uniform(sm.wfirst[p.j]) + (uniform(sm.wcount[p.j]) - 1 - p.k) * kBQB;
+  };
   auto hb_of = [&](const StepPos& p) { return (int64_t)(b * P.hq + g * P.G + p.hs); };
-  StageA<D> sa;
-  StageB<D> sb;
-  {
-    const int32_t r0 = row_of(cur);
-    stage_load_a<D>(A, P, K, P.q[sm.wseg[cur.j]], hb_of(cur), r0, tid, sa);
-    stage_load_b<D>(A, P, P.q[sm.wseg[cur.j]], hb_of(cur), r0, tid, sb);
-    stage_store_a<D>(sm, 0, tid, sa);
-    stage_store_b<D>(sm, 0, tid, sb);
-  }
+  auto cq_of = [&](const StepPos& p) { return (int64_t)P.q[uniform(sm.wseg[p.j])].tile0 * kBQ + row_of(p); };
+  stage<D>(A, P, K.kind, hb_of(cur), cq_of(cur), wave, lane, o, sm, 0);
+  wait_copies();
   __syncthreads();
+  StepPos nxt = total > 1 ? advance(cur) : cur;
+  if (total > 1) touch_l2<D>(A, P, hb_of(nxt), cq_of(nxt), wave, lane, sm);
   for (int32_t t = 0; t < total; ++t) {
-    const int BUF = t & 1;
-    const int32_t si = sm.wseg[cur.j];
-    const int32_t r0 = row_of(cur);
-    const bool more = t + 1 < total;
-    StepPos nxt = cur;
-    int32_t sn = si, rn = 0;
+    const int B = t & 1;
+    const bool more = t + 1 < total, more2 = t + 2 < total;
+    StepPos nxt2 = nxt;
     if (more) {
-      nxt = advance(cur);
-      sn = sm.wseg[nxt.j];
-      rn = row_of(nxt);
-      stage_load_a<D>(A, P, K, P.q[sn], hb_of(nxt), rn, tid, sa);
+      stage<D>(A, P, K.kind, hb_of(nxt), cq_of(nxt), wave, lane, o, sm, B ^ 1);
+      if (more2) {
+        nxt2 = advance(nxt);
+        touch_l2<D>(A, P, hb_of(nxt2), cq_of(nxt2), wave, lane, sm);
+      }
     }
     if constexpr (S_WAVE) {
       // no mask when every row of the step exists and sees every key of the tile
+      const QSeg& S = P.q[uniform(sm.wseg[cur.j])];
+      const int32_t r0 = row_of(cur);
       bool full = false;
-      if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= P.q[si].nrows)
-        full = row_bounds(P, P.q[si], r0).hi_clean >= kt1;
-      f16x8 pf[kNB][2];
-      s_phase_a<D>(sm, full, BUF, kw, lane, ql, hh, mysrc, c2, kvreg, pf);
-      if (more) stage_store_a<D>(sm, BUF ^ 1, tid, sa);
-      __syncthreads();  // P visible to the P-waves
-      if (more) stage_load_b<D>(A, P, P.q[sn], hb_of(nxt), rn, tid, sb);
-      s_phase_b<D>(sm, BUF, ql, hh, pf, acc);
+      if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= S.nrows)
+        full = row_bounds(P, S, r0).hi_clean >= kt1;
+      f16x8 pf[kRB][kKB][2];
+      if (full)
+        s_phase_a<D, true>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
+      else
+        s_phase_a<D, false>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
+      barrier_lds();  // P visible to the P-waves
+      rows_contract<D>(sm.dot[B], ql, o, pf, acc);  // dV^T += dO^T P
     } else {
-      f32x16 pacc[kNB];
-      p_phase_a<D>(sm, BUF, ql, hh, kvreg, pacc);
-      if (more) stage_store_a<D>(sm, BUF ^ 1, tid, sa);
-      __syncthreads();  // P from the S-waves
-      if (more) stage_load_b<D>(A, P, P.q[sn], hb_of(nxt), rn, tid, sb);
-      p_phase_b<D>(sm, BUF, kw, lane, ql, hh, pacc, acc);
+      f32x16 pacc[kRB][kKB];
+      p_phase_a<D>(sm, B, ql, kvreg, o, pacc);
+      barrier_lds();  // P from the S-waves
+      f16x8 dsf[kRB][kKB][2];
+      p_phase_ds<D>(sm, B, kw, lane, hh, pacc, dsf);
+      rows_contract<D>(sm.qt[B], ql, o, dsf, acc);  // dK^T += Q^T dS
     }
-    if (more) stage_store_b<D>(sm, BUF ^ 1, tid, sb);
-    __syncthreads();
+    if (more2)
+      wait_all_but(touches_of(kTouchTotal<D>, wave));  // leave only the prefetches in flight
+    else
+      wait_copies();
+    __syncthreads();  // the next step's copies have landed; this step's reads are done
     cur = nxt;
+    nxt = nxt2;
+  }
+  wait_copies();
+}
+
+// One role of the workgroup on its key tile: this wave's 64 keys in
+// registers (K for the S-wave, V for the P-wave), the query walk, and the
+// write-out of its gradient (dV or dK).  Each role keeps its accumulators
+// in one place for the whole walk.
+template <int D, bool S_WAVE>
+__device__ __forceinline__ void dkdv_role(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, const KSeg& K, int b,
+                                          int g, int32_t c, int32_t kvalid, int32_t kt1, int wave, int kw, int lane,
+                                          int ql, int hh, const int32_t (&mysrc)[kKB], const bool (&key_ok)[kKB],
+                                          int32_t nseg, int32_t total, const LaneOff<D>& o) {
+  bf16x8 kvreg[kKB][D / 16];
+  {
+    const uint16_t* src = S_WAVE ? A.kn : A.vn;
+    const int64_t nb = ((int64_t)(b * P.hkv + g) * P.nkc + c + kw * kKW + ql) * D + hh * 8;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kvreg[kb][ks] = ld16<bf16x8>(src + nb + kb * 32 * D + ks * 16);
+  }
+  f32x16 acc[D / 32][kKB];  // dV^T (S-wave) or dK^T (P-wave)
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) acc[db][kb] = f32x16{};
+  if (total > 0)
+    dkdv_walk<D, S_WAVE>(P, A, sm, K, b, g, kvalid, kt1, wave, kw, lane, ql, hh, mysrc, nseg, total, o, kvreg, acc);
+  agpr_settle();
+  const float f = S_WAVE ? 1.f : P.scale;
+#pragma unroll
+  for (int kb = 0; kb < kKB; ++kb) {
+    if (!key_ok[kb]) continue;
+    float* dst;
+    int64_t rowoff;
+    if (K.kind == KIND_CLEAN) {
+      dst = S_WAVE ? A.dv_clean : A.dk_clean;
+      rowoff = (((int64_t)b * P.L + mysrc[kb]) * P.hkv + g) * D;
+    } else {
+      dst = S_WAVE ? A.dv_corr : A.dk_corr;
+      rowoff = (((int64_t)b * P.n_corr_rows + mysrc[kb]) * P.hkv + g) * D;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        f32x4* pd = reinterpret_cast<f32x4*>(dst + rowoff + db * 32 + crow(i, hh));
+        f32x4 cur4 = *pd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur4[e] += f * acc[db][kb][i + e];
+        *pd = cur4;
+      }
   }
 }
 
 template <int D>
 __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int b, int g, int32_t ktile) {
-  static_assert(kThreads >= kBQB, "one thread per row stages the per-row data");
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
-  const int kw = wave % kPairs;       // which 32 keys of the tile
-  const bool s_wave = wave < kPairs;  // S-wave (dV) or P-wave (dK)
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave % kPairs;  // which 64 keys of the tile
   int32_t kseg, koff;
   ktile_locate(P, ktile, &kseg, &koff);
   const KSeg K = P.k[kseg];
@@ -356,21 +510,15 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
   const int32_t kt0 = K.t0 + koff;                 // first source row
   const int32_t kt1 = kt0 + kvalid;
   const int32_t c = K.c0 + koff;                   // compact start
-  const int32_t mykey = kw * 32 + ql;
-  const bool key_ok = mykey < kvalid;
-  const int32_t mysrc = key_ok ? kt0 + mykey : INT_MIN;
-
-  // this wave's 32 keys as B operands: K (S-wave) or V (P-wave)
-  bf16x8 kvreg[D / 16];
-  {
-    const uint16_t* src = s_wave ? A.kn : A.vn;
-    const int64_t nb = ((int64_t)(b * P.hkv + g) * P.nkc + c + kw * 32 + ql) * D;
+  int32_t mysrc[kKB];
+  bool key_ok[kKB];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kvreg[ks] = ld16<bf16x8>(src + nb + ks * 16 + hh * 8);
+  for (int kb = 0; kb < kKB; ++kb) {
+    const int32_t key = kw * kKW + kb * 32 + ql;
+    key_ok[kb] = key < kvalid;
+    mysrc[kb] = key_ok[kb] ? kt0 + key : INT_MIN;
   }
-  f32x16 acc[D / 32];  // dV^T (S-wave) or dK^T (P-wave)
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  const LaneOff<D> o = lane_offsets<D>(wave, lane);
 
   if (tid == 0) {
     int32_t nseg = 0, per = 0;
@@ -392,35 +540,10 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
   __syncthreads();
   const int32_t nseg = sm.wn;
   const int32_t total = sm.wper * P.G;
-
-  if (total > 0) {
-    if (s_wave)
-      dkdv_walk<D, true>(P, A, sm, K, b, g, kvalid, kt1, tid, kw, lane, ql, hh, mysrc, nseg, total, kvreg, acc);
-    else
-      dkdv_walk<D, false>(P, A, sm, K, b, g, kvalid, kt1, tid, kw, lane, ql, hh, mysrc, nseg, total, kvreg, acc);
-  }
-  if (key_ok) {
-    float* dst;
-    int64_t rowoff;
-    if (K.kind == KIND_CLEAN) {
-      dst = s_wave ? A.dv_clean : A.dk_clean;
-      rowoff = (((int64_t)b * P.L + mysrc) * P.hkv + g) * D;
-    } else {
-      dst = s_wave ? A.dv_corr : A.dk_corr;
-      rowoff = (((int64_t)b * P.n_corr_rows + mysrc) * P.hkv + g) * D;
-    }
-    const float f = s_wave ? 1.f : P.scale;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        f32x4* pd = reinterpret_cast<f32x4*>(dst + rowoff + db * 32 + crow(i, hh));
-        f32x4 cur4 = *pd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cur4[e] += f * acc[db][i + e];
-        *pd = cur4;
-      }
-  }
+  if (wave < kPairs)
+    dkdv_role<D, true>(P, A, sm, K, b, g, c, kvalid, kt1, wave, kw, lane, ql, hh, mysrc, key_ok, nseg, total, o);
+  else
+    dkdv_role<D, false>(P, A, sm, K, b, g, c, kvalid, kt1, wave, kw, lane, ql, hh, mysrc, key_ok, nseg, total, o);
 }
 
 template <int D>

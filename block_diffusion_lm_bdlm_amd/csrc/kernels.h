@@ -38,6 +38,8 @@ struct PackQArgs {
   _Float16* dot;
   float* lse2;         // [batch][hq][nqc] log2-scaled LSE; +inf on padding rows
   float* dc;           // [batch][hq][nqc] delta; 0 on padding rows
+  int32_t* vis;        // [4][nqc] visible source rows per compact row: [lo, hi) of the
+                       // clean keys, then [lo, hi) of the packed corrupted keys; 0 on padding
 };
 
 struct FwdArgs {
@@ -82,6 +84,7 @@ struct DkdvArgs {
   const _Float16* dot;
   const float* lse2;
   const float* dc;
+  const int32_t* vis;
   const uint16_t* kn;
   const uint16_t* vn;
   float* dk_clean;  // [batch][L][hkv][d], +=

@@ -8,7 +8,8 @@
 //          group of 16 rows is in perm16 order, the order in which an MFMA C
 //          tile delivers its rows as a B operand.
 //  pack_q: the same for the share's query side of the backward (Q, dO,
-//          natural and transposed), plus log2-scaled LSE and delta per row.
+//          natural and transposed), plus log2-scaled LSE and delta per row
+//          and each row's visible key interval per key kind.
 //  delta:  D_i = sum_t dO_i[t] O_i[t], the softmax backward's row term.
 // All three are bandwidth-bound copies; none changes a value except the
 // bf16 -> fp16 conversion of the transposed operands (exact for values in
@@ -122,6 +123,19 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
     }
     A.lse2[hb * P.nqc + c + tid] = l2;
     A.dc[hb * P.nqc + c + tid] = dd;
+    if (h == 0 && b == 0) {  // per compact row, the same for every head and batch
+      int32_t v[4] = {0, 0, 0, 0};
+      if (rr < S.nrows) {
+        const RowBounds rb = row_bounds(P, S, rr);
+        v[1] = rb.hi_clean;
+        if (S.kind == KIND_CORR) {
+          v[2] = rb.lo_loc;
+          v[3] = rb.hi_loc;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) A.vis[(int64_t)k * P.nqc + c + tid] = v[k];
+    }
   }
   __syncthreads();
   const int64_t tb = hb * D * P.nqc + (int64_t)c * D;  // tile c / kPT
