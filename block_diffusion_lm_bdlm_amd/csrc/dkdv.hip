@@ -24,8 +24,7 @@
 // per-row log2 LSE, D and visible key interval) go from global memory
 // straight into LDS through the load units (global_load_lds), double
 // buffered, into unpadded tiles whose 16-byte chunks are XOR-swizzled by
-// row, so the fragment reads are free of bank conflicts; the step after
-// next is touched into L2 meanwhile.
+// row, so the fragment reads are free of bank conflicts.
 // The walk runs back to front by position (all heads of the group at each
 // position): the last rows are seen by every key tile, so the workgroups
 // resident on one XCD stay on the same rows and share them through L2.
@@ -74,14 +73,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return ((int64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-// Waits for all but the N most recent copies (vector memory operations
-// complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_copies_but() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
-}
-
 // Barrier that orders this wave's LDS writes before its partners' reads,
 // without waiting for the copies still in flight.
 __device__ __forceinline__ void barrier_lds() {
@@ -109,7 +100,6 @@ struct __attribute__((aligned(16))) DkdvSmem {
   int32_t vhi[2][kBQB];
   // P from each S-wave to its P-wave, in the MFMA C-tile order of each lane
   _Float16 xchg[kPairs][kRB][kKB][2][64][8];
-  float touch[kWaves][64];  // landing slot of the L2 prefetches (never read)
   // steps of the walk: segment s contributes wcount[s] steps from row wfirst[s]
   int32_t wseg[kMaxQSeg], wfirst[kMaxQSeg], wcount[kMaxQSeg];
   int32_t wn, wper;
@@ -192,46 +182,6 @@ __device__ __forceinline__ void stage(const DkdvArgs& A, const Plan& P, int kkin
     case 3: copy4(A.vis + (int64_t)(2 * kkind + 1) * P.nqc + cq, lo, &sm.vhi[B][0]); break;
     default: break;
   }
-}
-
-// Touches every 128-byte line of a step's four tiles so that they are in
-// L2 when their copies are issued one step later; the 4 bytes per lane land
-// in a scratch slot of LDS.  Touch i covers 64 lines of tile i / (D / 64);
-// wave w issues touches w, w + kWaves, ...
-template <int D>
-constexpr int kTouchTotal = 4 * D / 64;
-__device__ __forceinline__ int touches_of(int total, int wave) {
-  return wave < total ? (total - wave + kWaves - 1) / kWaves : 0;
-}
-
-template <int D>
-__device__ __forceinline__ void touch_l2(const DkdvArgs& A, const Plan& P, int64_t hb, int64_t cq, int wave,
-                                         int lane, DkdvSmem<D>& sm) {
-  constexpr int PT = D / 64;  // touches per tile
-  const int64_t base = uniform64((hb * P.nqc + cq) * D);
-#pragma unroll
-  for (int i0 = 0; i0 < kTouchTotal<D>; i0 += kWaves) {
-    const int i = i0 + wave;
-    if (i >= kTouchTotal<D>) break;
-    const uint32_t off = (uint32_t)((i % PT) * 64 + lane) * 128;
-    switch (i / PT) {
-      case 0: copy4(A.qn + base, off, &sm.touch[wave][0]); break;
-      case 1: copy4(A.don + base, off, &sm.touch[wave][0]); break;
-      case 2: copy4(A.qt + base, off, &sm.touch[wave][0]); break;
-      default: copy4(A.dot + base, off, &sm.touch[wave][0]); break;
-    }
-  }
-}
-
-// Waits until only this wave's `n` most recent copies (its touches) are
-// still in flight.
-__device__ __forceinline__ void wait_all_but(int n) {
-  if (n >= 2)
-    wait_copies_but<2>();
-  else if (n == 1)
-    wait_copies_but<1>();
-  else
-    wait_copies();
 }
 
 // S-wave, first half of a step: S = Q K^T, then P = exp2(S c2 - LSE2) on
@@ -339,7 +289,8 @@ __device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const 
   }
 }
 
-// P-wave, second half: dS = P (dP - D) with P from its S-wave.
+// P-wave, second half: dS = P (dP - D) with P from its S-wave (dP - D is
+// rounded to fp16 before the product; dS is an fp16 operand either way).
 template <int D>
 __device__ __forceinline__ void p_phase_ds(DkdvSmem<D>& sm, int B, int kw, int lane, int hh,
                                            const f32x16 (&pacc)[kRB][kKB], f16x8 (&dsf)[kRB][kKB][2]) {
@@ -352,11 +303,11 @@ __device__ __forceinline__ void p_phase_ds(DkdvSmem<D>& sm, int B, int kw, int l
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         const f16x8 p = ld16<f16x8>(&sm.xchg[kw][rb][kb][ss][lane][0]);
+        // dP - D in fp32, then the product with P in packed fp16
+        f16x8 t;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float dd = e < 4 ? d0[e & 3] : d1[e & 3];
-          dsf[rb][kb][ss][e] = (_Float16)((float)p[e] * (pacc[rb][kb][ss * 8 + e] - dd));
-        }
+        for (int e = 0; e < 8; ++e) t[e] = (_Float16)(pacc[rb][kb][ss * 8 + e] - (e < 4 ? d0[e & 3] : d1[e & 3]));
+        dsf[rb][kb][ss] = p * t;
       }
     }
 }
@@ -400,18 +351,13 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
   stage<D>(A, P, K.kind, hb_of(cur), cq_of(cur), wave, lane, o, sm, 0);
   wait_copies();
   __syncthreads();
-  StepPos nxt = total > 1 ? advance(cur) : cur;
-  if (total > 1) touch_l2<D>(A, P, hb_of(nxt), cq_of(nxt), wave, lane, sm);
   for (int32_t t = 0; t < total; ++t) {
     const int B = t & 1;
-    const bool more = t + 1 < total, more2 = t + 2 < total;
-    StepPos nxt2 = nxt;
+    const bool more = t + 1 < total;
+    StepPos nxt = cur;
     if (more) {
+      nxt = advance(cur);
       stage<D>(A, P, K.kind, hb_of(nxt), cq_of(nxt), wave, lane, o, sm, B ^ 1);
-      if (more2) {
-        nxt2 = advance(nxt);
-        touch_l2<D>(A, P, hb_of(nxt2), cq_of(nxt2), wave, lane, sm);
-      }
     }
     if constexpr (S_WAVE) {
       // no mask when every row of the step exists and sees every key of the tile
@@ -435,15 +381,10 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
       p_phase_ds<D>(sm, B, kw, lane, hh, pacc, dsf);
       rows_contract<D>(sm.qt[B], ql, o, dsf, acc);  // dK^T += Q^T dS
     }
-    if (more2)
-      wait_all_but(touches_of(kTouchTotal<D>, wave));  // leave only the prefetches in flight
-    else
-      wait_copies();
+    wait_copies();
     __syncthreads();  // the next step's copies have landed; this step's reads are done
     cur = nxt;
-    nxt = nxt2;
   }
-  wait_copies();
 }
 
 // One role of the workgroup on its key tile: this wave's 64 keys in
