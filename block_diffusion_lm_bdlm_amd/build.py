@@ -15,12 +15,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["bdattn.cpp", "fwd.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
-# Per-file code generation options.  dkdv.hip keeps its long-lived
-# accumulators in AGPRs (inline-assembly products) and asks for every other
+# Per-file code generation options.  The backward kernels keep their long-lived
+# accumulators in AGPRs (inline-assembly products) and ask for every other
 # matrix product in the VGPR form, so the scores feeding vector code need no
-# AGPR -> VGPR copies.  Its global->LDS copies set M0 in inline assembly; the
-# file makes no other use of M0, so the reserved-register warning is off.
-EXTRA = {"dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]}
+# AGPR -> VGPR copies.  Their global->LDS copies set M0 in inline assembly; the
+# files make no other use of M0, so the reserved-register warning is off.
+_BWD = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]
+EXTRA = {"dkdv.hip": _BWD, "bwd.hip": _BWD}
 ARCH = os.environ.get("BDATTN_ARCH", "gfx950")
 
 

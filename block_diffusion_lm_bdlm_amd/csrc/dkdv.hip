@@ -32,6 +32,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "stage.h"
 
 namespace bd {
 
@@ -44,49 +45,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRB = kBQB / 32;        // 32-row MFMA blocks per step
 constexpr int kKB = kKW / 32;         // 32-key MFMA blocks per wave
 static_assert(kBKB % kKW == 0 && kKW % 32 == 0, "whole 32-key blocks per wave");
-static_assert(kBQB == 64, "one lane per row stages the per-row data; 64-row transposed tiles");
+static_assert(kBQB == kTileRows, "one lane per row stages the per-row data; 64-row tiles");
 static_assert(kWaves >= 4, "the four per-row arrays are staged one per wave");
 
-typedef __attribute__((address_space(3))) const void lds_void;
-
-// Copies 16 (4) bytes per lane from global memory at sbase + voff into LDS
-// at `lds` + 16 lane (4 lane); sbase and lds are the same for the whole wave.
-// Written as inline assembly so the compiler does not order the copy
-// against unrelated LDS reads; completion is awaited explicitly
-// (wait_copies) before the barrier that publishes the data.  M0 (the LDS
-// address) needs one wait state before the copy reads it.
-__device__ __forceinline__ void copy16(const void* sbase, uint32_t voff, const void* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(la)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void copy4(const void* sbase, uint32_t voff, const void* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(la)
-               : "memory", "m0");
-}
-// Marks a value that is the same in every lane as such (scalar registers).
-__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)x);
-  const int32_t hi = __builtin_amdgcn_readfirstlane((int32_t)(x >> 32));
-  return ((int64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-// Barrier that orders this wave's LDS writes before its partners' reads,
-// without waiting for the copies still in flight.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Staged tiles are unpadded; 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r).  The LDS serves a 128-bit read 16 lanes (256 bytes)
-// at a time, so the 16 rows one fragment read touches must land on 16
-// different 16-byte bank groups: swz(r) = r & 15 for 256-byte rows and
-// (r >> 1) & 7 for 128-byte rows (two rows share a 256-byte bank line).
 template <int D>
 struct __attribute__((aligned(16))) DkdvSmem {
   static constexpr int TILE = kBQB * D;  // elements per staged tile
@@ -104,59 +65,6 @@ struct __attribute__((aligned(16))) DkdvSmem {
   int32_t wseg[kMaxQSeg], wfirst[kMaxQSeg], wcount[kMaxQSeg];
   int32_t wn, wper;
 };
-
-template <int NC>  // chunks per row: 16 (256-byte rows) or 8 (128-byte rows)
-__host__ __device__ constexpr int swz(int r) {
-  static_assert(NC == 16 || NC == 8, "rows of 128 or 256 bytes");
-  return NC == 16 ? (r & 15) : ((r >> 1) & 7);
-}
-
-// Per-lane element offsets into the swizzled tiles.  A fragment read takes
-// logical chunk 2 k + hh (k-th 16-element step, lane half hh) of row
-// 32 m + ql; swz(32 m + ql) = swz(ql).
-template <int D>
-struct LaneOff {
-  int nat[D / 16];     // natural rows (D / 8 chunks)
-  int tr[kBQB / 16];   // transposed rows (8 chunks)
-  uint32_t dn, dt;     // byte offsets of this lane's first copied chunk (natural, transposed)
-};
-
-template <int D>
-__device__ inline LaneOff<D> lane_offsets(int wave, int lane) {
-  constexpr int NCR = D / 8;  // chunks per natural row
-  static_assert((kWaves * 64 / NCR) % 16 == 0 && (kWaves * 8) % 16 == 0,
-                "a wave's later copy blocks keep its rows' swizzle");
-  const int ql = lane & 31, hh = lane >> 5;
-  LaneOff<D> o;
-#pragma unroll
-  for (int k = 0; k < D / 16; ++k) o.nat[k] = ((2 * k + hh) ^ swz<NCR>(ql)) * 8;
-#pragma unroll
-  for (int k = 0; k < kBQB / 16; ++k) o.tr[k] = ((2 * k + hh) ^ swz<8>(ql)) * 8;
-  const int p = wave * 64 + lane;  // physical chunk of the wave's first 1 KB block
-  const int row = p / NCR;
-  o.dn = (uint32_t)(row * D + ((p % NCR) ^ swz<NCR>(row)) * 8) * 2;
-  const int d = p / 8;
-  o.dt = (uint32_t)(d * kBQB + ((p % 8) ^ swz<8>(d)) * 8) * 2;
-  return o;
-}
-
-// acc += A B with the accumulator held in AGPRs for the whole walk.  The
-// product is written as inline assembly so the accumulator stays in the
-// AGPRs while every other product (compiled in the VGPR form) feeds vector
-// code directly.  Inputs come from LDS reads and vector instructions, whose
-// results the hardware interlocks for the matrix core; the accumulator is
-// read back only after agpr_settle().
-__device__ __forceinline__ void mfma_f16_agpr(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Wait states before vector code may read an accumulator that a product
-// just wrote (more than a 32x32x16 product's 16 passes).
-__device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
-
-// Fragment reads kept in flight ahead of the products that consume them;
-// scheduling barriers pin this order (the compiler otherwise sinks each
-// read to its first use).
-constexpr int kAhead = 6;
 
 // Issues the copies of one step (64 rows from compact row cq of head hb)
 // into buffer B.  Every wave copies its share of each tile.
@@ -459,7 +367,7 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
     key_ok[kb] = key < kvalid;
     mysrc[kb] = key_ok[kb] ? kt0 + key : INT_MIN;
   }
-  const LaneOff<D> o = lane_offsets<D>(wave, lane);
+  const LaneOff<D> o = lane_offsets<D, kWaves>(wave, lane);
 
   if (tid == 0) {
     int32_t nseg = 0, per = 0;
