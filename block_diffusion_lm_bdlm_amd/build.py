@@ -15,13 +15,14 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["bdattn.cpp", "fwd.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
-# Per-file code generation options.  The backward kernels keep their long-lived
-# accumulators in AGPRs (inline-assembly products) and ask for every other
-# matrix product in the VGPR form, so the scores feeding vector code need no
-# AGPR -> VGPR copies.  Their global->LDS copies set M0 in inline assembly; the
-# files make no other use of M0, so the reserved-register warning is off.
-_BWD = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]
-EXTRA = {"dkdv.hip": _BWD, "bwd.hip": _BWD}
+# Per-file code generation options for the bf16 kernels: every matrix
+# product the compiler emits uses the VGPR form, so scores feed vector code
+# with no AGPR -> VGPR copies; the backward kernels keep their long-lived
+# accumulators in AGPRs through inline-assembly products.  The global->LDS
+# copies set M0 in inline assembly; these files make no other use of M0, so
+# the reserved-register warning is off.
+_MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]
+EXTRA = {"dkdv.hip": _MFMA_VGPR, "bwd.hip": _MFMA_VGPR, "fwd.hip": _MFMA_VGPR}
 ARCH = os.environ.get("BDATTN_ARCH", "gfx950")
 
 

@@ -58,36 +58,13 @@ __device__ __forceinline__ void dq_stage(const DqArgs& A, const Plan& P, int b, 
   }
 }
 
-// S^T (S-wave) or dP^T (P-wave) of one key tile: two 32-key blocks of
-// tile[key][d] times the lane's row held in registers; fragment f = (ks, kb).
-template <int D>
-__device__ __forceinline__ void dq_scores(const uint16_t* tile, int ql, const bf16x8 (&row)[D / 16],
-                                          const LaneOff<D>& o, f32x16 (&acc)[2]) {
-  constexpr int NF = 2 * (D / 16);
-  const uint16_t* tb = tile + ql * D;
-  bf16x8 fr[NF];
-#pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    if (f + kAhead < NF) {
-      const int h = f + kAhead;
-      fr[h] = ld16<bf16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
-    }
-    const int kb = f & 1, ks = f >> 1;
-    acc[kb] = mfma_bf16(fr[f], row[ks], ks ? acc[kb] : f32x16{});
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // S-wave: S^T, then P^T = exp2(S^T c2 - LSE2) on visible pairs, to LDS.
 template <int D, bool FULL>
 __device__ __forceinline__ void dq_s_phase(DqSmem<D>& sm, int B, int pw, int lane, int ql, int hh, int32_t c,
                                            int32_t vlo, int32_t vhi, float c2, float lse2,
                                            const bf16x8 (&qreg)[D / 16], const LaneOff<D>& o) {
   f32x16 sacc[2];
-  dq_scores<D>(sm.k[B], ql, qreg, o, sacc);
+  scores_2kb<D>(sm.k[B], ql, qreg, o, sacc);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f16x8 pf[2];
@@ -177,7 +154,7 @@ __device__ __forceinline__ void dq_walk(const Plan& P, const DqArgs& A, DqSmem<D
       barrier_lds();  // P^T visible to the P-waves
     } else {
       f32x16 pacc[2];
-      dq_scores<D>(sm.v[B], ql, qreg, o, pacc);  // dP^T = V dO^T
+      scores_2kb<D>(sm.v[B], ql, qreg, o, pacc);  // dP^T = V dO^T
       barrier_lds();  // P^T from the S-waves
       dq_p_phase<D>(sm, B, pw, lane, ql, rowval, pacc, o, dqacc);
     }

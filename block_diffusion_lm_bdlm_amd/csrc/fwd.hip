@@ -9,10 +9,12 @@
 // bf16 kernel: a workgroup of 4 waves owns a 128-row query tile (32 rows
 // per wave, the rows held as the B operand of S^T = K Q^T) and walks the
 // key tiles of 64 keys that any of its rows can see.  K tiles (natural) and
-// V^T tiles (fp16) are staged through LDS, double buffered.  A key tile that
+// V^T tiles (fp16) go from global memory straight into LDS
+// (global_load_lds), double buffered, as swizzled tiles.  A key tile that
 // no row sees is never visited; a tile every row sees fully skips the mask.
 #include "device.h"
 #include "kernels.h"
+#include "stage.h"
 #include "walk.h"
 
 namespace bd {
@@ -21,54 +23,36 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+constexpr int kFwdWaves = 4;
+static_assert(kBK == kTileRows, "key tiles are staged as 64-row tiles");
+
 template <int D>
 struct __attribute__((aligned(16))) FwdSmem {
-  static constexpr int KS = D + 8;    // K row stride (bf16 elements)
-  static constexpr int VS = kBK + 8;  // V^T row stride (fp16 elements)
-  uint16_t k[2][kBK * KS];
-  _Float16 v[2][D * VS];
+  static constexpr int TILE = kBK * D;  // elements per staged tile
+  uint16_t k[2][TILE];                  // natural bf16 [key][d]
+  _Float16 vt[2][TILE];                 // transposed fp16 [d][key], perm16 keys
 };
 
+// Issues the copies of key tile c (compact start) into buffer B.
 template <int D>
-__device__ inline void fwd_load_tile(const FwdArgs& A, const Plan& P, int b, int g, int c, int tid,
-                                     u32x4 (&kr)[D / 32], u32x4 (&vr)[D / 32]) {
-  const uint16_t* kb = A.kn + ((int64_t)(b * P.hkv + g) * P.nkc + c) * D;
+__device__ __forceinline__ void fwd_stage(const FwdArgs& A, const Plan& P, int b, int g, int32_t c, int wave,
+                                          const LaneOff<D>& o, FwdSmem<D>& sm, int B) {
+  constexpr int PER = kBK * D / 512 / kFwdWaves;  // 1 KB blocks per wave per tile
+  const int64_t base = uniform64(((int64_t)(b * P.hkv + g) * P.nkc + c) * D);  // natural and transposed alike
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int ch = tid + 256 * j;  // chunk of 8 elements
-    const int key = ch / (D / 8), dc = ch % (D / 8);
-    kr[j] = ldg16(kb + key * D + dc * 8);
-  }
-  const _Float16* vb = A.vt + (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // [D][64] tile
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int ch = tid + 256 * j;
-    const int d = ch / (kBK / 8), kc = ch % (kBK / 8);
-    vr[j] = ldg16(vb + d * kBK + kc * 8);
-  }
-}
-
-template <int D>
-__device__ inline void fwd_store_tile(FwdSmem<D>& sm, int buf, int tid, const u32x4 (&kr)[D / 32],
-                                      const u32x4 (&vr)[D / 32]) {
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int ch = tid + 256 * j;
-    const int key = ch / (D / 8), dc = ch % (D / 8);
-    *reinterpret_cast<u32x4*>(&sm.k[buf][key * FwdSmem<D>::KS + dc * 8]) = kr[j];
-  }
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int ch = tid + 256 * j;
-    const int d = ch / (kBK / 8), kc = ch % (kBK / 8);
-    *reinterpret_cast<u32x4*>(&sm.v[buf][d * FwdSmem<D>::VS + kc * 8]) = vr[j];
+  for (int j = 0; j < PER; ++j) {
+    const int blk = (wave + kFwdWaves * j) * 512;  // elements
+    const int64_t e = base + (int64_t)j * kFwdWaves * 512;
+    copy16(A.kn + e, o.dn, &sm.k[B][blk]);
+    copy16(A.vt + e, o.dt, &sm.vt[B][blk]);
   }
 }
 
 template <int D>
 __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b, int h, int g,
                          int32_t tile) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int wave = uniform(tid >> 6);
   const QSeg S = P.q[seg_of_tile(P, tile)];
   const int32_t r0 = (tile - S.tile0) * kBQ;
   const int32_t n = min(kBQ, S.nrows - r0);
@@ -86,6 +70,7 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
 
   const RowBounds rb = row_bounds(P, S, r0 + rc);
   const KeyWalk w = keywalk_build(P, S, r0, r0 + n - 1);
+  const LaneOff<D> o = lane_offsets<D, kFwdWaves>(wave, lane);
 
   const float c2 = P.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
@@ -94,14 +79,13 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
   if (w.total > 0) {
-    u32x4 kr[D / 32], vr[D / 32];
     {
       int32_t c, ri;
       bool fu;
       keywalk_at(w, 0, &c, &ri, &fu);
-      fwd_load_tile<D>(A, P, b, g, c, tid, kr, vr);
-      fwd_store_tile<D>(sm, 0, tid, kr, vr);
+      fwd_stage<D>(A, P, b, g, c, wave, o, sm, 0);
     }
+    wait_copies();
     __syncthreads();
     for (int32_t t = 0; t < w.total; ++t) {
       const int buf = t & 1;
@@ -112,21 +96,11 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
         int32_t cn, rn;
         bool fn;
         keywalk_at(w, t + 1, &cn, &rn, &fn);
-        fwd_load_tile<D>(A, P, b, g, cn, tid, kr, vr);
+        fwd_stage<D>(A, P, b, g, cn, wave, o, sm, buf ^ 1);
       }
       // S^T = K Q^T for two blocks of 32 keys
       f32x16 sacc[2];
-      const uint16_t* kbase = sm.k[buf];
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-      // consecutive products feed different accumulators (independent chains)
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = ld16<bf16x8>(kbase + (kb * 32 + ql) * FwdSmem<D>::KS + ks * 16 + hh * 8);
-          sacc[kb] = mfma_bf16(a, qreg[ks], sacc[kb]);
-        }
+      scores_2kb<D>(sm.k[buf], ql, qreg, o, sacc);
       if (!full) {
         int32_t vlo, vhi;
         compact_range(P.k[ri], rb, clean, &vlo, &vhi);
@@ -164,20 +138,27 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       }
       m_run = m_new;
-      // O^T += V^T P^T
-      const _Float16* vbase = sm.v[buf];
+      // O^T += V^T P^T; fragment f = (s, db), s = 16-key step
+      {
+        constexpr int NDB = D / 32, NF = (kBK / 16) * NDB;
+        const _Float16* tb = sm.vt[buf] + ql * kBK;
+        f16x8 fr[NF];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBK + o.tr[f / NDB]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const f16x8 a =
-                ld16<f16x8>(vbase + (db * 32 + ql) * FwdSmem<D>::VS + kb * 32 + ss * 16 + hh * 8);
-            oacc[db] = mfma_f16(a, pf[kb][ss], oacc[db]);
+        for (int f = 0; f < NF; ++f) {
+          if (f + kAhead < NF) {
+            const int hf = f + kAhead;
+            fr[hf] = ld16<f16x8>(tb + (hf % NDB) * 32 * kBK + o.tr[hf / NDB]);
           }
-      if (t + 1 < w.total) fwd_store_tile<D>(sm, buf ^ 1, tid, kr, vr);
-      __syncthreads();
+          const int s = f / NDB, db = f % NDB;
+          oacc[db] = mfma_f16(fr[f], pf[s >> 1][s & 1], oacc[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wait_copies();
+      __syncthreads();  // the next tile's copies have landed; this tile's reads are done
     }
   }
 
@@ -221,7 +202,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const Plan P, const Fw
   __shared__ FwdSmem<D> sm;
   const WgQ wg = decode_wg_q(P, blockIdx.x);
   fwd_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);
-  if (wg.tile_b >= 0) fwd_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_b);
+  if (wg.tile_b >= 0) {
+    __syncthreads();
+    fwd_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_b);
+  }
 }
 
 // ------------------------------------------------------------------ fp32

@@ -1,5 +1,5 @@
 // stage.h — staging of operand tiles in LDS and the matrix-core helpers
-// shared by the backward kernels.
+// shared by the bf16 kernels.
 //
 // Tiles go from global memory straight into LDS through the load units
 // (global_load_lds), one 1 KB block per wave instruction, and are read back
@@ -112,5 +112,29 @@ __device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7
 // scheduling barriers pin this order (the compiler otherwise sinks each
 // read to its first use).
 constexpr int kAhead = 6;
+
+// C^T blocks of one staged natural tile: acc[kb] = tile[kb*32 .. +32][:]
+// times the lane's row held in registers (B operand), for the two 32-row
+// blocks of a 64-row tile; fragment f = (ks, kb), kAhead reads in flight.
+template <int D>
+__device__ __forceinline__ void scores_2kb(const uint16_t* tile, int ql, const bf16x8 (&row)[D / 16],
+                                           const LaneOff<D>& o, f32x16 (&acc)[2]) {
+  constexpr int NF = 2 * (D / 16);
+  const uint16_t* tb = tile + ql * D;
+  bf16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) {
+      const int h = f + kAhead;
+      fr[h] = ld16<bf16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
+    }
+    const int kb = f & 1, ks = f >> 1;
+    acc[kb] = mfma_bf16(fr[f], row[ks], ks ? acc[kb] : f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 }  // namespace bd
