@@ -21,16 +21,20 @@ namespace bd {
 namespace {
 
 // ----------------------------------------------------------------- dQ
-// A workgroup owns a 128-row query tile of one head and runs 8 waves, two
-// per SIMD, in pairs that own the same 32 query rows:
-//   S-wave: Q in registers; S^T = K Q^T, P^T = exp(S^T - LSE) (masked),
-//           hands P^T to its partner through LDS.
-//   P-wave: dO in registers; dP^T = V dO^T, dS^T = P^T (dP^T - D),
-//           accumulates dQ^T += K^T dS^T in AGPRs; one writer per row.
-// Each key tile's K, V (natural bf16) and K^T (fp16) go from global memory
-// straight into LDS (global_load_lds), double buffered, as swizzled tiles.
-constexpr int kDqWaves = 8;
+// A workgroup owns a 128-row query tile of one head and runs 2 waves, one
+// per SIMD (two workgroups per CU), each owning 64 rows (two 32-row
+// blocks).  A wave holds its rows' Q and dO (B operands) and its dQ^T
+// accumulators in AGPRs and, per key tile of 64 keys,
+//   S^T = K Q^T,  P^T = exp(S^T - LSE) (masked),  dP^T = V dO^T,
+//   dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T,
+// reading each K, V and K^T fragment from LDS once for both row blocks.
+// K and V (natural bf16) go from global memory straight into LDS
+// (global_load_lds), double buffered; K^T (fp16) is single buffered and
+// copied after the tile's last product has read it.
+constexpr int kDqWaves = 2;
 constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = kBQ / kDqWaves;  // query rows per wave
+static_assert(kDqRows == 64, "two 32-row blocks per wave");
 static_assert(kBK == kTileRows, "key tiles are staged as 64-row tiles");
 
 template <int D>
@@ -38,69 +42,132 @@ struct __attribute__((aligned(16))) DqSmem {
   static constexpr int TILE = kBK * D;  // elements per staged tile
   uint16_t k[2][TILE];                  // natural bf16 [key][d]
   uint16_t v[2][TILE];
-  _Float16 kt[2][TILE];                 // transposed fp16 [d][key], perm16 keys
-  _Float16 xchg[4][2][2][64][8];        // P^T per pair, 32-key block, k-step, lane
+  _Float16 kt[TILE];                    // transposed fp16 [d][key], perm16 keys
 };
 
-// Issues the copies of key tile c (compact start) into buffer B.
 template <int D>
-__device__ __forceinline__ void dq_stage(const DqArgs& A, const Plan& P, int b, int g, int32_t c, int wave,
-                                         const LaneOff<D>& o, DqSmem<D>& sm, int B) {
-  constexpr int PER = kBK * D / 512 / kDqWaves;  // 1 KB blocks per wave per tile
-  const int64_t base = uniform64(((int64_t)(b * P.hkv + g) * P.nkc + c) * D);  // natural and transposed alike
+constexpr int kDqPer = kBK * D / 512 / kDqWaves;  // 1 KB blocks per wave per tile
+
+template <int D>
+__device__ __forceinline__ int64_t dq_tile_base(const Plan& P, int b, int g, int32_t c) {
+  return uniform64(((int64_t)(b * P.hkv + g) * P.nkc + c) * D);  // natural and transposed alike
+}
+
+// Copies of key tile c: K and V into buffer B.
+template <int D>
+__device__ __forceinline__ void dq_stage_kv(const DqArgs& A, const Plan& P, int b, int g, int32_t c, int wave,
+                                            const LaneOff<D>& o, DqSmem<D>& sm, int B) {
+  const int64_t base = dq_tile_base<D>(P, b, g, c);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int blk = (wave + kDqWaves * j) * 512;  // elements
+  for (int j = 0; j < kDqPer<D>; ++j) {
+    const int blk = (wave + kDqWaves * j) * 512;
     const int64_t e = base + (int64_t)j * kDqWaves * 512;
-    copy16(A.kn + e, o.dn, &sm.k[B][blk]);
-    copy16(A.vn + e, o.dn, &sm.v[B][blk]);
-    copy16(A.kt + e, o.dt, &sm.kt[B][blk]);
+    copy16(A.kn + e, o.dn[j & 1], &sm.k[B][blk]);
+    copy16(A.vn + e, o.dn[j & 1], &sm.v[B][blk]);
   }
 }
-
-// S-wave: S^T, then P^T = exp2(S^T c2 - LSE2) on visible pairs, to LDS.
-template <int D, bool FULL>
-__device__ __forceinline__ void dq_s_phase(DqSmem<D>& sm, int B, int pw, int lane, int ql, int hh, int32_t c,
-                                           int32_t vlo, int32_t vhi, float c2, float lse2,
-                                           const bf16x8 (&qreg)[D / 16], const LaneOff<D>& o) {
-  f32x16 sacc[2];
-  scores_2kb<D>(sm.k[B], ql, qreg, o, sacc);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f16x8 pf[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = fmaf(sacc[kb][i], c2, -lse2);
-      if constexpr (!FULL) {
-        const int32_t key = c + kb * 32 + crow(i, hh);
-        x = (key >= vlo && key < vhi) ? x : -INFINITY;
-      }
-      pf[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(x);
-    }
-    *reinterpret_cast<f16x8*>(&sm.xchg[pw][kb][0][lane][0]) = pf[0];
-    *reinterpret_cast<f16x8*>(&sm.xchg[pw][kb][1][lane][0]) = pf[1];
-  }
-}
-
-// P-wave, after the exchange: dS^T = P^T (dP^T - D) (dP - D rounded to fp16
-// before the product) and dQ^T += K^T dS^T; fragment f = (s, db).
+// Copies of key tile c: K^T.
 template <int D>
-__device__ __forceinline__ void dq_p_phase(DqSmem<D>& sm, int B, int pw, int lane, int ql, float dval,
-                                           const f32x16 (&pacc)[2], const LaneOff<D>& o,
-                                           f32x16 (&dqacc)[D / 32]) {
-  f16x8 dsf[2][2];
+__device__ __forceinline__ void dq_stage_kt(const DqArgs& A, const Plan& P, int b, int g, int32_t c, int wave,
+                                            const LaneOff<D>& o, DqSmem<D>& sm) {
+  const int64_t base = dq_tile_base<D>(P, b, g, c);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int j = 0; j < kDqPer<D>; ++j) {
+    const int blk = (wave + kDqWaves * j) * 512;
+    const int64_t e = base + (int64_t)j * kDqWaves * 512;
+    copy16(A.kt + e, o.dt, &sm.kt[blk]);
+  }
+}
+
+// acc[rb][kb] = tile[kb*32 .. +32][:] times row block rb's registers (AGPR
+// B operands), for both key and row blocks; each fragment (ks, kb) is read
+// once and feeds both row blocks.
+template <int D>
+__device__ __forceinline__ void dq_products(const uint16_t* tile, int ql, const bf16x8 (&rows)[2][D / 16],
+                                            const LaneOff<D>& o, f32x16 (&acc)[2][2]) {
+  constexpr int NF = 2 * (D / 16);
+  const uint16_t* tb = tile + ql * D;
+  bf16x8 fr[NF];
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const f16x8 p = ld16<f16x8>(&sm.xchg[pw][kb][ss][lane][0]);
-      f16x8 t;
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = (_Float16)(pacc[kb][ss * 8 + e] - dval);
-      dsf[kb][ss] = p * t;
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) {
+      const int h = f + kAhead;
+      fr[h] = ld16<bf16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
     }
+    const int kb = f & 1, ks = f >> 1;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (ks == 0)
+        acc[rb][kb] = mfma_bf16_bagpr0(fr[f], rows[rb][ks]);
+      else
+        mfma_bf16_bagpr(acc[rb][kb], fr[f], rows[rb][ks]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+struct DqRows {
+  float lse2[2], dval[2];
+  int32_t vlo[2], vhi[2];  // visible compact keys of this tile (masked tiles)
+};
+
+// One key tile of the wave's walk (buffers B for K, V; K^T single).
+template <int D>
+__device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t c, const DqRows& rw, float c2,
+                                        int ql, int hh, const bf16x8 (&qreg)[2][D / 16],
+                                        const bf16x8 (&doreg)[2][D / 16], const LaneOff<D>& o,
+                                        f32x16 (&dqacc)[2][D / 32], int nkv) {
+  // S^T and P^T = exp2(S^T c2 - LSE2)
+  f32x16 sc[2][2];
+  dq_products<D>(sm.k[B], ql, qreg, o, sc);
+  mfma_settle();
+  if (!full) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t key = c + kb * 32 + crow(i, hh);
+          if (key < rw.vlo[rb] || key >= rw.vhi[rb]) sc[rb][kb][i] = -INFINITY;
+        }
+  }
+  f16x8 pf[2][2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pf[rb][kb][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[rb][kb][i], c2, -rw.lse2[rb]));
+  // dP^T, then dS^T = P^T (dP^T - D) (dP - D rounded to fp16 before the product)
+  f32x16 pc[2][2];
+  dq_products<D>(sm.v[B], ql, doreg, o, pc);
+  mfma_settle();
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        f16x8 t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (_Float16)(pc[rb][kb][ss * 8 + e] - rw.dval[rb]);
+        pf[rb][kb][ss] = pf[rb][kb][ss] * t;
+      }
+  // K^T of this tile has landed for every wave
+  if (nkv > 0)
+    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * kDqPer<D>) & 15) | (((2 * kDqPer<D>) >> 4) << 14));
+  else
+    wait_copies();
+  __syncthreads();
+  mfma_settle();
+  // dQ^T += K^T dS^T; fragment f = (s, db) feeds both row blocks
   constexpr int NDB = D / 32, NF = (kBK / 16) * NDB;
-  const _Float16* tb = sm.kt[B] + ql * kBK;
+  const _Float16* tb = sm.kt + ql * kBK;
   f16x8 fr[NF];
 #pragma unroll
   for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBK + o.tr[f / NDB]);
@@ -111,80 +178,88 @@ __device__ __forceinline__ void dq_p_phase(DqSmem<D>& sm, int B, int pw, int lan
       const int h = f + kAhead;
       fr[h] = ld16<f16x8>(tb + (h % NDB) * 32 * kBK + o.tr[h / NDB]);
     }
-    const int s = f / NDB, db = f % NDB;
-    mfma_f16_agpr(dqacc[db], fr[f], dsf[s >> 1][s & 1]);
+    const int sk = f / NDB, db = f % NDB;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) mfma_f16_agpr(dqacc[rb][db], fr[f], pf[rb][sk >> 1][sk & 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One role's walk over the key tiles; both roles run the same barriers.
-template <int D, bool S_WAVE>
-__device__ __forceinline__ void dq_walk(const Plan& P, const DqArgs& A, DqSmem<D>& sm, const KeyWalk& w,
-                                        const RowBounds& rb, bool clean, int b, int g, int wave, int pw, int lane,
-                                        int ql, int hh, const bf16x8 (&qreg)[D / 16], float rowval,
-                                        const LaneOff<D>& o, f32x16 (&dqacc)[D / 32]) {
-  const float c2 = P.scale_log2;
-  {
-    int32_t c, ri;
-    bool fu;
-    keywalk_at(w, 0, &c, &ri, &fu);
-    dq_stage<D>(A, P, b, g, c, wave, o, sm, 0);
-  }
-  wait_copies();
-  __syncthreads();
-  for (int32_t t = 0; t < w.total; ++t) {
-    const int B = t & 1;
-    int32_t c, ri;
-    bool full;
-    keywalk_at(w, t, &c, &ri, &full);
-    if (t + 1 < w.total) {
-      int32_t cn, rn;
-      bool fn;
-      keywalk_at(w, t + 1, &cn, &rn, &fn);
-      dq_stage<D>(A, P, b, g, cn, wave, o, sm, B ^ 1);
-    }
-    if constexpr (S_WAVE) {
-      if (full) {
-        dq_s_phase<D, true>(sm, B, pw, lane, ql, hh, c, 0, 0, c2, rowval, qreg, o);
-      } else {
-        int32_t vlo, vhi;
-        compact_range(P.k[ri], rb, clean, &vlo, &vhi);
-        dq_s_phase<D, false>(sm, B, pw, lane, ql, hh, c, vlo, vhi, c2, rowval, qreg, o);
-      }
-      barrier_lds();  // P^T visible to the P-waves
-    } else {
-      f32x16 pacc[2];
-      scores_2kb<D>(sm.v[B], ql, qreg, o, pacc);  // dP^T = V dO^T
-      barrier_lds();  // P^T from the S-waves
-      dq_p_phase<D>(sm, B, pw, lane, ql, rowval, pacc, o, dqacc);
-    }
-    wait_copies();
-    __syncthreads();  // the next tile's copies have landed; this tile's reads are done
-  }
-}
+template <int D>
+__device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, int h, int g, int32_t tile) {
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int wave = uniform(tid >> 6);
+  const QSeg S = P.q[seg_of_tile(P, tile)];
+  const int32_t r0 = (tile - S.tile0) * kBQ;
+  const int32_t n = min(kBQ, S.nrows - r0);
+  const bool clean = S.kind == KIND_CLEAN;
+  const int64_t hb = (int64_t)(b * P.hq + h);
 
-template <int D, bool S_WAVE>
-__device__ __forceinline__ void dq_role(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, int h, int g,
-                                        int wave, int pw, int lane, int ql, int hh, const QSeg& S, int32_t r0,
-                                        int32_t n, int32_t rq, int64_t crow_q) {
-  bf16x8 qreg[D / 16];  // Q (S-wave) or dO (P-wave) of this lane's row as B operands
-  {
-    const uint16_t* src = S_WAVE ? A.qn : A.don;
+  // Q and dO of this lane's two rows (B operands, kept in AGPRs)
+  bf16x8 qreg[2][D / 16], doreg[2][D / 16];
+  DqRows rw;
+  RowBounds rbd[2];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = ld16<bf16x8>(src + crow_q * D + ks * 16 + hh * 8);
+  for (int rb = 0; rb < 2; ++rb) {
+    const int32_t rq = wave * kDqRows + rb * 32 + ql;
+    const int64_t cr = hb * P.nqc + (int64_t)tile * kBQ + rq;  // compact (zero-padded) row
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qreg[rb][ks] = ld16<bf16x8>(A.qn + cr * D + ks * 16 + hh * 8);
+      doreg[rb][ks] = ld16<bf16x8>(A.don + cr * D + ks * 16 + hh * 8);
+      keep_in_agpr(qreg[rb][ks]);
+      keep_in_agpr(doreg[rb][ks]);
+    }
+    rw.lse2[rb] = A.lse2[cr];
+    rw.dval[rb] = A.dc[cr];
+    rbd[rb] = row_bounds(P, S, r0 + min(rq, n - 1));
   }
-  const float rowval = S_WAVE ? A.lse2[crow_q] : A.dc[crow_q];  // LSE2 (S-wave) or D (P-wave)
-  const RowBounds rb = row_bounds(P, S, r0 + min(rq, n - 1));
   const KeyWalk w = keywalk_build(P, S, r0, r0 + n - 1);
   const LaneOff<D> o = lane_offsets<D, kDqWaves>(wave, lane);
-  f32x16 dqacc[D / 32];
+  const float c2 = P.scale_log2;
+  f32x16 dqacc[2][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
-  if (w.total > 0)
-    dq_walk<D, S_WAVE>(P, A, sm, w, rb, S.kind == KIND_CLEAN, b, g, wave, pw, lane, ql, hh, qreg, rowval, o,
-                       dqacc);
-  if constexpr (!S_WAVE) {
-    agpr_settle();
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dqacc[rb][db] = f32x16{};
+
+  if (w.total > 0) {
+    {
+      int32_t c, ri;
+      bool fu;
+      keywalk_at(w, 0, &c, &ri, &fu);
+      dq_stage_kv<D>(A, P, b, g, c, wave, o, sm, 0);
+      dq_stage_kt<D>(A, P, b, g, c, wave, o, sm);
+    }
+    wait_copies();
+    __syncthreads();
+    for (int32_t t = 0; t < w.total; ++t) {
+      const int B = t & 1;
+      int32_t c, ri;
+      bool full;
+      keywalk_at(w, t, &c, &ri, &full);
+      const bool more = t + 1 < w.total;
+      int32_t cn = c;
+      if (more) {
+        int32_t rn;
+        bool fn;
+        keywalk_at(w, t + 1, &cn, &rn, &fn);
+        dq_stage_kv<D>(A, P, b, g, cn, wave, o, sm, B ^ 1);
+      }
+      if (!full) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) compact_range(P.k[ri], rbd[rb], clean, &rw.vlo[rb], &rw.vhi[rb]);
+      }
+      dq_step<D>(sm, B, full, c, rw, c2, ql, hh, qreg, doreg, o, dqacc, more ? 1 : 0);
+      wait_copies();
+      __syncthreads();  // the next tile's K, V have landed; this tile's K^T reads are done
+      if (more) dq_stage_kt<D>(A, P, b, g, cn, wave, o, sm);
+    }
+  }
+  agpr_settle();
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int32_t rq = wave * kDqRows + rb * 32 + ql;
     if (rq < n) {
       const int32_t row = S.row0 + r0 + rq;
       float* dp = A.dq + (((int64_t)b * P.R + row) * P.hq + h) * D;
@@ -195,7 +270,7 @@ __device__ __forceinline__ void dq_role(const Plan& P, const DqArgs& A, DqSmem<D
           f32x4* p4 = reinterpret_cast<f32x4*>(dp + db * 32 + crow(i, hh));
           f32x4 cur = *p4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) cur[e] += P.scale * dqacc[db][i + e];
+          for (int e = 0; e < 4; ++e) cur[e] += P.scale * dqacc[rb][db][i + e];
           *p4 = cur;
         }
     }
@@ -203,24 +278,8 @@ __device__ __forceinline__ void dq_role(const Plan& P, const DqArgs& A, DqSmem<D
 }
 
 template <int D>
-__device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, int h, int g, int32_t tile) {
-  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
-  const int wave = uniform(tid >> 6);
-  const int pw = wave & 3;  // which 32 rows of the tile
-  const QSeg S = P.q[seg_of_tile(P, tile)];
-  const int32_t r0 = (tile - S.tile0) * kBQ;
-  const int32_t n = min(kBQ, S.nrows - r0);
-  const int32_t rq = pw * 32 + ql;
-  const int64_t hb = (int64_t)(b * P.hq + h);
-  const int64_t crow_q = hb * P.nqc + (int64_t)tile * kBQ + rq;  // compact (zero-padded) row
-  if (wave < 4)
-    dq_role<D, true>(P, A, sm, b, h, g, wave, pw, lane, ql, hh, S, r0, n, rq, crow_q);
-  else
-    dq_role<D, false>(P, A, sm, b, h, g, wave, pw, lane, ql, hh, S, r0, n, rq, crow_q);
-}
-
-template <int D>
-__global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(const Plan P, const DqArgs A) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kDqThreads, kDqThreads), amdgpu_waves_per_eu(1, 1)))
+void dq_kernel(const Plan P, const DqArgs A) {
   __shared__ DqSmem<D> sm;
   const WgQ wg = decode_wg_q(P, blockIdx.x);
   dq_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);

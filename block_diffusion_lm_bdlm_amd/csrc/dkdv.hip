@@ -77,8 +77,8 @@ __device__ __forceinline__ void stage(const DkdvArgs& A, const Plan& P, int kkin
   for (int j = 0; j < PER; ++j) {
     const int blk = (wave + kWaves * j) * 512;  // elements
     const int64_t e = base + (int64_t)j * kWaves * 512;
-    copy16(A.qn + e, o.dn, &sm.q[B][blk]);
-    copy16(A.don + e, o.dn, &sm.dO[B][blk]);
+    copy16(A.qn + e, o.dn[j & 1], &sm.q[B][blk]);
+    copy16(A.don + e, o.dn[j & 1], &sm.dO[B][blk]);
     copy16(A.qt + e, o.dt, &sm.qt[B][blk]);
     copy16(A.dot + e, o.dt, &sm.dot[B][blk]);
   }

@@ -43,7 +43,7 @@ __device__ __forceinline__ void fwd_stage(const FwdArgs& A, const Plan& P, int b
   for (int j = 0; j < PER; ++j) {
     const int blk = (wave + kFwdWaves * j) * 512;  // elements
     const int64_t e = base + (int64_t)j * kFwdWaves * 512;
-    copy16(A.kn + e, o.dn, &sm.k[B][blk]);
+    copy16(A.kn + e, o.dn[j & 1], &sm.k[B][blk]);
     copy16(A.vt + e, o.dt, &sm.vt[B][blk]);
   }
 }

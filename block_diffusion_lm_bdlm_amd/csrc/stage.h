@@ -71,25 +71,30 @@ template <int D>
 struct LaneOff {
   int nat[D / 16];          // natural rows (D / 8 chunks)
   int tr[kTileRows / 16];   // transposed rows (8 chunks)
-  uint32_t dn, dt;          // byte offsets of this lane's first copied chunk (natural, transposed)
+  uint32_t dn[2];           // byte offsets of this lane's chunk in its even / odd copy blocks (natural)
+  uint32_t dt;              // byte offset of this lane's chunk in every copy block (transposed)
 };
 
 // Offsets for a workgroup of NW waves whose wave w copies 1 KB blocks
-// w, w + NW, ... of every tile.
+// w, w + NW, ... of every tile (the j-th of them with dn[j & 1]).
 template <int D, int NW>
 __device__ inline LaneOff<D> lane_offsets(int wave, int lane) {
   constexpr int NCR = D / 8;  // chunks per natural row
-  static_assert((NW * 64 / NCR) % 16 == 0 && (NW * 8) % 16 == 0,
-                "a wave's later copy blocks keep its rows' swizzle");
+  static_assert((2 * NW * 64 / NCR) % 16 == 0 && (NW * 8) % 16 == 0,
+                "a wave's copy blocks two apart keep its rows' swizzle");
   const int ql = lane & 31, hh = lane >> 5;
   LaneOff<D> o;
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) o.nat[k] = ((2 * k + hh) ^ swz<NCR>(ql)) * 8;
 #pragma unroll
   for (int k = 0; k < kTileRows / 16; ++k) o.tr[k] = ((2 * k + hh) ^ swz<8>(ql)) * 8;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = (wave + NW * j) * 64 + lane;  // physical chunk in the wave's j-th 1 KB block
+    const int row = p / NCR;
+    o.dn[j] = (uint32_t)(row * D + ((p % NCR) ^ swz<NCR>(row)) * 8 - (NW * j * 64 / NCR) * D) * 2;
+  }
   const int p = wave * 64 + lane;  // physical chunk of the wave's first 1 KB block
-  const int row = p / NCR;
-  o.dn = (uint32_t)(row * D + ((p % NCR) ^ swz<NCR>(row)) * 8) * 2;
   const int d = p / 8;
   o.dt = (uint32_t)(d * kTileRows + ((p % 8) ^ swz<8>(d)) * 8) * 2;
   return o;
@@ -104,6 +109,24 @@ __device__ inline LaneOff<D> lane_offsets(int wave, int lane) {
 __device__ __forceinline__ void mfma_f16_agpr(f32x16& acc, const f16x8& a, const f16x8& b) {
   asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// acc = A B (first) or acc += A B with B held in AGPRs and the result in
+// VGPRs, for operands that stay in registers for a whole walk.
+__device__ __forceinline__ f32x16 mfma_bf16_bagpr0(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_bf16_bagpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// Pins a register value in AGPRs (no instruction).
+template <typename T>
+__device__ __forceinline__ void keep_in_agpr(T& x) {
+  asm volatile("" : "+a"(x));
+}
+// Wait states between products whose results vector code reads next, or
+// between vector writes and products that read them (covers both).
+__device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 // Wait states before vector code may read an accumulator that a product
 // just wrote (more than a 32x32x16 product's 16 passes).
 __device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
