@@ -114,13 +114,49 @@ struct DqRows {
   int32_t vlo[2], vhi[2];  // visible compact keys of this tile (masked tiles)
 };
 
-// One key tile of the wave's walk (buffers B for K, V; K^T single).
+// dS^T chunk (kb, ss) of both row blocks: P^T (dP^T - D), with dP - D
+// rounded to fp16 before the product; written over P^T.
+__device__ __forceinline__ void dq_ds_chunk(int kb, int ss, const f32x16 (&pc)[2][2], const float (&dval)[2],
+                                            f16x8 (&pf)[2][2][2]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    f16x8 t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = (_Float16)(pc[rb][kb][ss * 8 + e] - dval[rb]);
+    pf[rb][kb][ss] = pf[rb][kb][ss] * t;
+  }
+}
+
+// Piece q of NP of the dS^T chunk (kb, ss) of both row blocks: row block
+// q / (NP / 2), elements of the 8 in slice q % (NP / 2).
+template <int NP>
+__device__ __forceinline__ void dq_ds_piece(int q, int kb, int ss, const f32x16 (&pc)[2][2], const float (&dval)[2],
+                                            f16x8 (&pf)[2][2][2]) {
+  constexpr int H = NP / 2, W = 8 / H;  // pieces per row block, elements per piece
+  static_assert(8 % H == 0 && W % 2 == 0, "pieces of whole fp16 pairs");
+  const int rb = q / H, e0 = (q % H) * W;
+#pragma unroll
+  for (int e = e0; e < e0 + W; e += 2) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 t = {(_Float16)(pc[rb][kb][ss * 8 + e] - dval[rb]), (_Float16)(pc[rb][kb][ss * 8 + e + 1] - dval[rb])};
+    f16x2 p = {pf[rb][kb][ss][e], pf[rb][kb][ss][e + 1]};
+    const f16x2 r = p * t;
+    pf[rb][kb][ss][e] = r[0];
+    pf[rb][kb][ss][e + 1] = r[1];
+  }
+}
+
+// One key tile of the wave's walk (buffers B for K, V; K^T single).  The
+// vector work of each stage runs between the matrix products of the next:
+// the exponentials between the dP^T products, each dS^T chunk between the
+// dQ^T products of the previous chunk.
 template <int D>
 __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t c, const DqRows& rw, float c2,
                                         int ql, int hh, const bf16x8 (&qreg)[2][D / 16],
                                         const bf16x8 (&doreg)[2][D / 16], const LaneOff<D>& o,
                                         f32x16 (&dqacc)[2][D / 32], int nkv) {
-  // S^T and P^T = exp2(S^T c2 - LSE2)
+  constexpr int NF = 2 * (D / 16);  // K or V fragments (ks, kb)
+  // S^T
   f32x16 sc[2][2];
   dq_products<D>(sm.k[B], ql, qreg, o, sc);
   mfma_settle();
@@ -135,29 +171,42 @@ __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t
           if (key < rw.vlo[rb] || key >= rw.vhi[rb]) sc[rb][kb][i] = -INFINITY;
         }
   }
+  // dP^T = V dO^T, with P^T = exp2(S^T c2 - LSE2) between the products
   f16x8 pf[2][2][2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pf[rb][kb][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[rb][kb][i], c2, -rw.lse2[rb]));
-  // dP^T, then dS^T = P^T (dP^T - D) (dP - D rounded to fp16 before the product)
   f32x16 pc[2][2];
-  dq_products<D>(sm.v[B], ql, doreg, o, pc);
-  mfma_settle();
+  {
+    constexpr int PE = 64 / NF;  // probabilities per fragment
+    const uint16_t* tb = sm.v[B] + ql * D;
+    bf16x8 fr[NF];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        f16x8 t;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (_Float16)(pc[rb][kb][ss * 8 + e] - rw.dval[rb]);
-        pf[rb][kb][ss] = pf[rb][kb][ss] * t;
+    for (int f = 0; f < NF; ++f) {
+      if (f + kAhead < NF) {
+        const int h = f + kAhead;
+        fr[h] = ld16<bf16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
       }
+      const int kb = f & 1, ks = f >> 1;
+      // each product is followed by half of this fragment's probabilities
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        if (ks == 0)
+          pc[rb][kb] = mfma_bf16_bagpr0(fr[f], doreg[rb][ks]);
+        else
+          mfma_bf16_bagpr(pc[rb][kb], fr[f], doreg[rb][ks]);
+#pragma unroll
+        for (int e = rb * (PE / 2); e < (rb + 1) * (PE / 2); ++e) {
+          const int x = f * PE + e, prb = x >> 5, pkb = (x >> 4) & 1, i = x & 15;
+          pf[prb][pkb][i >> 3][i & 7] =
+              (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[prb][pkb][i], c2, -rw.lse2[prb]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  mfma_settle();
+  dq_ds_chunk(0, 0, pc, rw.dval, pf);
   // K^T of this tile has landed for every wave
   if (nkv > 0)
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * kDqPer<D>) & 15) | (((2 * kDqPer<D>) >> 4) << 14));
@@ -165,23 +214,33 @@ __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t
     wait_copies();
   __syncthreads();
   mfma_settle();
-  // dQ^T += K^T dS^T; fragment f = (s, db) feeds both row blocks
-  constexpr int NDB = D / 32, NF = (kBK / 16) * NDB;
+  // dQ^T += K^T dS^T; fragment f = (s, db) feeds both row blocks, chunk s + 1
+  // of dS^T is formed during group s
+  constexpr int NDB = D / 32, NT = (kBK / 16) * NDB;
   const _Float16* tb = sm.kt + ql * kBK;
-  f16x8 fr[NF];
+  f16x8 fr[NT];
 #pragma unroll
   for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBK + o.tr[f / NDB]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    if (f + kAhead < NF) {
+  for (int f = 0; f < NT; ++f) {
+    if (f + kAhead < NT) {
       const int h = f + kAhead;
       fr[h] = ld16<f16x8>(tb + (h % NDB) * 32 * kBK + o.tr[h / NDB]);
     }
     const int sk = f / NDB, db = f % NDB;
+    if (db == 0 && sk > 0) mfma_settle_short();
+    // each product is followed by a quarter of the next chunk's dS^T (one
+    // row block, four of its eight elements)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) mfma_f16_agpr(dqacc[rb][db], fr[f], pf[rb][sk >> 1][sk & 1]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int rb = 0; rb < 2; ++rb) {
+      mfma_f16_agpr(dqacc[rb][db], fr[f], pf[rb][sk >> 1][sk & 1]);
+      if (sk + 1 < kBK / 16) {
+        const int nk = sk + 1, q = db * 2 + rb;  // quarter q of 2 * NDB pieces
+        dq_ds_piece<2 * NDB>(q, nk >> 1, nk & 1, pc, rw.dval, pf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 

@@ -127,6 +127,8 @@ __device__ __forceinline__ void keep_in_agpr(T& x) {
 // Wait states between products whose results vector code reads next, or
 // between vector writes and products that read them (covers both).
 __device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+// Wait states between vector writes and a product that reads them.
+__device__ __forceinline__ void mfma_settle_short() { asm volatile("s_nop 3"); }
 // Wait states before vector code may read an accumulator that a product
 // just wrote (more than a 32x32x16 product's 16 passes).
 __device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
