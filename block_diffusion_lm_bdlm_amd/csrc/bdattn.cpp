@@ -165,7 +165,7 @@ struct BwdWs {
   uint16_t *kn, *vn;
   _Float16* kt;
   uint16_t *qn, *don;
-  _Float16 *qt, *dot;
+  _Float16 *qh, *doh;
   float *lse2, *dc;
   int32_t* vis;
 };
@@ -192,8 +192,8 @@ size_t carve_bwd(const Plan& P, char* base, BwdWs* w) {
   t.kt = cv.take<_Float16>(nk);
   t.qn = cv.take<uint16_t>(nq);
   t.don = cv.take<uint16_t>(nq);
-  t.qt = cv.take<_Float16>(nq);
-  t.dot = cv.take<_Float16>(nq);
+  t.qh = cv.take<_Float16>(nq);
+  t.doh = cv.take<_Float16>(nq);
   t.lse2 = cv.take<float>(nr);
   t.dc = cv.take<float>(nr);
   t.vis = cv.take<int32_t>((size_t)4 * P.nqc);
@@ -438,7 +438,7 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
     e = timed(K_DELTA, s, [&] { return launch_delta(P, da, s); });
     if (e != hipSuccess) return BDATTN_EHIP;
   }
-  PackQArgs pq{targ(q_clean), targ(q_corr), targ(d_o), lse_final, delta, ws.qn, ws.don, ws.qt, ws.dot,
+  PackQArgs pq{targ(q_clean), targ(q_corr), targ(d_o), lse_final, delta, ws.qn, ws.don, ws.qh, ws.doh,
                ws.lse2, ws.dc, ws.vis};
   e = timed(K_PACK_Q, s, [&] { return launch_pack_q(P, pq, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
@@ -454,7 +454,7 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   pk.kt = ws.kt;
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DkdvArgs ka{ws.qn, ws.don, ws.qt, ws.dot, ws.lse2, ws.dc, ws.vis, ws.kn, ws.vn,
+  DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kn, ws.vn,
               dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc};
   e = timed(K_DKDV, s, [&] { return launch_dkdv(P, ka, s); });
   if (e != hipSuccess) return BDATTN_EHIP;

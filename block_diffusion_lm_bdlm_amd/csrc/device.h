@@ -60,4 +60,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float((uint32_t)u << 16);
 }
 
+// Eight bf16 values (as loaded, two per dword) to fp16 through fp32; exact
+// for values in the half range above its subnormals.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4& v) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)bf16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+  return r;
+}
+
 }  // namespace bd

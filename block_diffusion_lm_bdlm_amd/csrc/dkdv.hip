@@ -19,12 +19,15 @@
 // each LDS fragment feed two products but need one wave per SIMD, which
 // measured slower.)
 // The workgroup walks every query row (of every query head of the group)
-// that sees its keys, in steps of 64 rows.  Each step's operands (natural Q,
-// dO for S and dP; transposed fp16 Q^T, dO^T for the contractions over rows;
-// per-row log2 LSE, D and visible key interval) go from global memory
-// straight into LDS through the load units (global_load_lds), double
-// buffered, into unpadded tiles whose 16-byte chunks are XOR-swizzled by
-// row, so the fragment reads are free of bank conflicts.
+// that sees its keys, in steps of 64 rows.  Each step's operands (Q and dO
+// as fp16 rows; per-row log2 LSE, D and visible key interval) go from
+// global memory straight into LDS through the load units (global_load_lds),
+// double buffered, into unpadded tiles whose 16-byte chunks are
+// XOR-swizzled by row.  S and dP read the tiles along their rows; the
+// contractions over rows (dV, dK) read the same tiles across their rows
+// with the transposing LDS read, so each operand is staged once.  All
+// products run in fp16 (K and V are converted once on load; Q and dO come
+// converted): the values are those of the bf16 inputs.
 // The walk runs back to front by position (all heads of the group at each
 // position): the last rows are seen by every key tile, so the workgroups
 // resident on one XCD stay on the same rows and share them through L2.
@@ -51,10 +54,8 @@ static_assert(kWaves >= 4, "the four per-row arrays are staged one per wave");
 template <int D>
 struct __attribute__((aligned(16))) DkdvSmem {
   static constexpr int TILE = kBQB * D;  // elements per staged tile
-  uint16_t q[2][TILE];                   // natural bf16 [row][d]
-  uint16_t dO[2][TILE];
-  _Float16 qt[2][TILE];                  // transposed fp16 [d][row], perm16 rows
-  _Float16 dot[2][TILE];
+  _Float16 q[2][TILE];                   // fp16 [row][d]
+  _Float16 dO[2][TILE];
   float lse2[2][kBQB];
   float dc[2][kBQB];
   int32_t vlo[2][kBQB];  // row sees key sources [vlo, vhi) of the tile's kind
@@ -77,10 +78,8 @@ __device__ __forceinline__ void stage(const DkdvArgs& A, const Plan& P, int kkin
   for (int j = 0; j < PER; ++j) {
     const int blk = (wave + kWaves * j) * 512;  // elements
     const int64_t e = base + (int64_t)j * kWaves * 512;
-    copy16(A.qn + e, o.dn[j & 1], &sm.q[B][blk]);
-    copy16(A.don + e, o.dn[j & 1], &sm.dO[B][blk]);
-    copy16(A.qt + e, o.dt, &sm.qt[B][blk]);
-    copy16(A.dot + e, o.dt, &sm.dot[B][blk]);
+    copy16(A.qh + e, o.dn[j & 1], &sm.q[B][blk]);
+    copy16(A.doh + e, o.dn[j & 1], &sm.dO[B][blk]);
   }
   const uint32_t lo = (uint32_t)lane * 4;
   switch (wave) {
@@ -97,26 +96,26 @@ __device__ __forceinline__ void stage(const DkdvArgs& A, const Plan& P, int kkin
 // contraction over rows.
 template <int D, bool FULL>
 __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int lane, int ql, int hh,
-                                          const int32_t (&mysrc)[kKB], float c2, const bf16x8 (&kreg)[kKB][D / 16],
+                                          const int32_t (&mysrc)[kKB], float c2, const f16x8 (&kreg)[kKB][D / 16],
                                           const LaneOff<D>& o, f16x8 (&pf)[kRB][kKB][2]) {
   constexpr int NKS = D / 16;
-  const uint16_t* qb = &sm.q[B][ql * D];
+  const _Float16* qb = &sm.q[B][ql * D];
   f32x16 sacc[kRB][kKB];
   // fragment f = (rb, ks); kAhead reads stay in flight ahead of the products
   constexpr int NF = kRB * NKS;
-  bf16x8 fr[NF];
+  f16x8 fr[NF];
 #pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(qb + (f / NKS) * 32 * D + o.nat[f % NKS]);
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(qb + (f / NKS) * 32 * D + o.nat[f % NKS]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f + kAhead < NF) {
       const int g = f + kAhead;
-      fr[g] = ld16<bf16x8>(qb + (g / NKS) * 32 * D + o.nat[g % NKS]);
+      fr[g] = ld16<f16x8>(qb + (g / NKS) * 32 * D + o.nat[g % NKS]);
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
-      sacc[f / NKS][kb] = mfma_bf16(fr[f], kreg[kb][f % NKS], f % NKS ? sacc[f / NKS][kb] : f32x16{});
+      sacc[f / NKS][kb] = mfma_f16(fr[f], kreg[kb][f % NKS], f % NKS ? sacc[f / NKS][kb] : f32x16{});
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -150,22 +149,22 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
 }
 
 // Contraction over the step's rows: acc^T[d][key] += T^T[d][row] X[row][key]
-// with T^T a transposed tile and X (P or dS) in registers.
+// with T a staged row tile (read across its rows) and X (P or dS) in
+// registers.
 template <int D>
-__device__ __forceinline__ void rows_contract(const _Float16* tile, int ql, const LaneOff<D>& o,
+__device__ __forceinline__ void rows_contract(const _Float16* tile, const LaneOff<D>& o,
                                               const f16x8 (&x)[kRB][kKB][2], f32x16 (&acc)[D / 32][kKB]) {
-  const _Float16* tb = tile + ql * kBQB;
   // fragment f = (s, db); kAhead reads stay in flight ahead of the products
   constexpr int NDB = D / 32, NF = (kBQB / 16) * NDB;
   f16x8 fr[NF];
 #pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBQB + o.tr[f / NDB]);
+  for (int f = 0; f < kAhead; ++f) fr[f] = tr_frag<D>(tile + (f / NDB) * 16 * D, o, f % NDB);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f + kAhead < NF) {
       const int g = f + kAhead;
-      fr[g] = ld16<f16x8>(tb + (g % NDB) * 32 * kBQB + o.tr[g / NDB]);
+      fr[g] = tr_frag<D>(tile + (g / NDB) * 16 * D, o, g % NDB);
     }
     const int s = f / NDB, db = f % NDB;
 #pragma unroll
@@ -176,23 +175,23 @@ __device__ __forceinline__ void rows_contract(const _Float16* tile, int ql, cons
 
 // P-wave, first half of a step: dP = dO V^T.
 template <int D>
-__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const bf16x8 (&vreg)[kKB][D / 16],
+__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const f16x8 (&vreg)[kKB][D / 16],
                                           const LaneOff<D>& o, f32x16 (&pacc)[kRB][kKB]) {
-  const uint16_t* ob = &sm.dO[B][ql * D];
+  const _Float16* ob = &sm.dO[B][ql * D];
   constexpr int NKS = D / 16, NF = kRB * NKS;
-  bf16x8 fr[NF];
+  f16x8 fr[NF];
 #pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(ob + (f / NKS) * 32 * D + o.nat[f % NKS]);
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(ob + (f / NKS) * 32 * D + o.nat[f % NKS]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f + kAhead < NF) {
       const int g = f + kAhead;
-      fr[g] = ld16<bf16x8>(ob + (g / NKS) * 32 * D + o.nat[g % NKS]);
+      fr[g] = ld16<f16x8>(ob + (g / NKS) * 32 * D + o.nat[g % NKS]);
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
-      pacc[f / NKS][kb] = mfma_bf16(fr[f], vreg[kb][f % NKS], f % NKS ? pacc[f / NKS][kb] : f32x16{});
+      pacc[f / NKS][kb] = mfma_f16(fr[f], vreg[kb][f % NKS], f % NKS ? pacc[f / NKS][kb] : f32x16{});
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -232,7 +231,7 @@ template <int D, bool S_WAVE>
 __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, const KSeg& K, int b,
                                           int g, int32_t kvalid, int32_t kt1, int wave, int kw, int lane, int ql,
                                           int hh, const int32_t (&mysrc)[kKB], int32_t nseg, int32_t total,
-                                          const LaneOff<D>& o, const bf16x8 (&kvreg)[kKB][D / 16],
+                                          const LaneOff<D>& o, const f16x8 (&kvreg)[kKB][D / 16],
                                           f32x16 (&acc)[D / 32][kKB]) {
   const float c2 = P.scale_log2;
   // Walk back to front by position: the k-th step from the end of every
@@ -280,14 +279,14 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
       else
         s_phase_a<D, false>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
       barrier_lds();  // P visible to the P-waves
-      rows_contract<D>(sm.dot[B], ql, o, pf, acc);  // dV^T += dO^T P
+      rows_contract<D>(sm.dO[B], o, pf, acc);  // dV^T += dO^T P
     } else {
       f32x16 pacc[kRB][kKB];
       p_phase_a<D>(sm, B, ql, kvreg, o, pacc);
       barrier_lds();  // P from the S-waves
       f16x8 dsf[kRB][kKB][2];
       p_phase_ds<D>(sm, B, kw, lane, hh, pacc, dsf);
-      rows_contract<D>(sm.qt[B], ql, o, dsf, acc);  // dK^T += Q^T dS
+      rows_contract<D>(sm.q[B], o, dsf, acc);  // dK^T += Q^T dS
     }
     wait_copies();
     __syncthreads();  // the next step's copies have landed; this step's reads are done
@@ -304,14 +303,15 @@ __device__ __forceinline__ void dkdv_role(const Plan& P, const DkdvArgs& A, Dkdv
                                           int g, int32_t c, int32_t kvalid, int32_t kt1, int wave, int kw, int lane,
                                           int ql, int hh, const int32_t (&mysrc)[kKB], const bool (&key_ok)[kKB],
                                           int32_t nseg, int32_t total, const LaneOff<D>& o) {
-  bf16x8 kvreg[kKB][D / 16];
+  f16x8 kvreg[kKB][D / 16];
   {
     const uint16_t* src = S_WAVE ? A.kn : A.vn;
     const int64_t nb = ((int64_t)(b * P.hkv + g) * P.nkc + c + kw * kKW + ql) * D + hh * 8;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kvreg[kb][ks] = ld16<bf16x8>(src + nb + kb * 32 * D + ks * 16);
+      for (int ks = 0; ks < D / 16; ++ks)
+        kvreg[kb][ks] = bf16x8_to_f16x8(ld16<u32x4>(src + nb + kb * 32 * D + ks * 16));
   }
   f32x16 acc[D / 32][kKB];  // dV^T (S-wave) or dK^T (P-wave)
 #pragma unroll

@@ -34,8 +34,8 @@ struct PackQArgs {
   const float* delta;  // [batch][R][hq]
   uint16_t* qn;        // [batch][hq][nqc][d] bf16
   uint16_t* don;
-  _Float16* qt;        // [batch][hq][nqc/64][d][64] fp16 tiles, perm16 groups of rows
-  _Float16* dot;
+  _Float16* qh;        // [batch][hq][nqc][d] fp16: the same values in half precision
+  _Float16* doh;
   float* lse2;         // [batch][hq][nqc] log2-scaled LSE; +inf on padding rows
   float* dc;           // [batch][hq][nqc] delta; 0 on padding rows
   int32_t* vis;        // [4][nqc] visible source rows per compact row: [lo, hi) of the
@@ -78,10 +78,8 @@ struct DqArgs {
 };
 
 struct DkdvArgs {
-  const uint16_t* qn;
-  const uint16_t* don;
-  const _Float16* qt;
-  const _Float16* dot;
+  const _Float16* qh;  // compact query side, fp16 natural
+  const _Float16* doh;
   const float* lse2;
   const float* dc;
   const int32_t* vis;

@@ -8,12 +8,12 @@
 //          group of 16 rows is in perm16 order, the order in which an MFMA C
 //          tile delivers its rows as a B operand.
 //  pack_q: the same for the share's query side of the backward (Q, dO,
-//          natural and transposed), plus log2-scaled LSE and delta per row
-//          and each row's visible key interval per key kind.
+//          natural bf16 and natural fp16), plus log2-scaled LSE and delta
+//          per row and each row's visible key interval per key kind.
 //  delta:  D_i = sum_t dO_i[t] O_i[t], the softmax backward's row term.
 // All three are bandwidth-bound copies; none changes a value except the
-// bf16 -> fp16 conversion of the transposed operands (exact for values in
-// the half range and above its subnormals).
+// bf16 -> fp16 conversions (exact for values in the half range and above
+// its subnormals).
 #include "device.h"
 #include "kernels.h"
 
@@ -22,7 +22,7 @@ namespace bd {
 namespace {
 
 constexpr int kPT = 64;  // rows per packing block = rows per transposed tile
-static_assert(kPT == kBK && kPT % kBQB == 0, "kernels read whole transposed tiles or aligned parts");
+static_assert(kPT == kBK, "consumers read whole transposed key tiles");
 
 template <int D>
 struct __attribute__((aligned(16))) PackSmem {
@@ -31,6 +31,7 @@ struct __attribute__((aligned(16))) PackSmem {
 };
 
 __device__ inline _Float16 bf16_to_f16(uint16_t u) { return (_Float16)bf16_to_f32(u); }
+
 
 // Writes the transposed, perm16-ordered fp16 tile [D][kPT] (contiguous) from LDS rows.
 template <int D>
@@ -85,7 +86,6 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
 
 template <int D>
 __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQArgs A) {
-  __shared__ PackSmem<D> sm;
   const int tid = threadIdx.x;
   const int32_t c = blockIdx.x * kPT;  // compact query row
   const int h = blockIdx.y, b = blockIdx.z;
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
     const int64_t nat = (hb * P.nqc + c + r) * D + dc;
     *reinterpret_cast<u32x4*>(A.qn + nat) = qv;
     *reinterpret_cast<u32x4*>(A.don + nat) = dv;
-    *reinterpret_cast<u32x4*>(&sm.a[r][dc]) = qv;
-    *reinterpret_cast<u32x4*>(&sm.b[r][dc]) = dv;
+    *reinterpret_cast<f16x8*>(A.qh + nat) = bf16x8_to_f16x8(qv);
+    *reinterpret_cast<f16x8*>(A.doh + nat) = bf16x8_to_f16x8(dv);
   }
   if (tid < kPT) {
     const int32_t rr = rbase + tid;
@@ -137,10 +137,6 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
       for (int k = 0; k < 4; ++k) A.vis[(int64_t)k * P.nqc + c + tid] = v[k];
     }
   }
-  __syncthreads();
-  const int64_t tb = hb * D * P.nqc + (int64_t)c * D;  // tile c / kPT
-  store_transposed<D>(sm.a, A.qt + tb, tid);
-  store_transposed<D>(sm.b, A.dot + tb, tid);
 }
 
 // D_i = dO_i . O_i: 16 lanes per (batch, row, head), 8 elements per lane.

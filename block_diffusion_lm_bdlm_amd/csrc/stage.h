@@ -3,7 +3,9 @@
 //
 // Tiles go from global memory straight into LDS through the load units
 // (global_load_lds), one 1 KB block per wave instruction, and are read back
-// as 32x32x16 MFMA fragments.
+// as 32x32x16 MFMA fragments, either along their rows (ds_read_b128) or
+// across them (ds_read_b64_tr_b16, which hands every lane one column of
+// four rows).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,14 +52,19 @@ __device__ __forceinline__ void barrier_lds() {
 
 
 // Staged tiles are unpadded; 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r).  The LDS serves a 128-bit read 16 lanes (256 bytes)
-// at a time, so the 16 rows one fragment read touches must land on 16
-// different 16-byte bank groups: swz(r) = r & 15 for 256-byte rows and
-// (r >> 1) & 7 for 128-byte rows (two rows share a 256-byte bank line).
+// position c ^ swz(r).  The LDS serves 256 bytes per cycle: a 128-bit read
+// 16 lanes at a time, a 64-bit read 32 lanes at a time.  A fragment read
+// along the rows touches one chunk of 16 consecutive rows; a transposed
+// read touches four chunks (64 bytes) of four consecutive rows, rows
+// 4i .. 4i+3.  Both land on distinct bank groups when swz maps the low two
+// row bits to the high chunk bits and bits 2-3 to the low chunk bits:
+//   256-byte rows: swz(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+//   128-byte rows (two rows per 256-byte bank line, told apart by r & 1):
+//                  swz(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
 template <int NC>  // chunks per row: 16 (256-byte rows) or 8 (128-byte rows)
 __host__ __device__ constexpr int swz(int r) {
   static_assert(NC == 16 || NC == 8, "rows of 128 or 256 bytes");
-  return NC == 16 ? (r & 15) : ((r >> 1) & 7);
+  return NC == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Per-lane element offsets into the swizzled tiles.  A fragment read takes
@@ -71,6 +78,7 @@ template <int D>
 struct LaneOff {
   int nat[D / 16];          // natural rows (D / 8 chunks)
   int tr[kTileRows / 16];   // transposed rows (8 chunks)
+  int ntr[2][D / 32];       // transposed reads of natural tiles: [half][32-column block]
   uint32_t dn[2];           // byte offsets of this lane's chunk in its even / odd copy blocks (natural)
   uint32_t dt;              // byte offset of this lane's chunk in every copy block (transposed)
 };
@@ -97,7 +105,37 @@ __device__ inline LaneOff<D> lane_offsets(int wave, int lane) {
   const int p = wave * 64 + lane;  // physical chunk of the wave's first 1 KB block
   const int d = p / 8;
   o.dt = (uint32_t)(d * kTileRows + ((p % 8) ^ swz<8>(d)) * 8) * 2;
+  // Transposed read of a natural tile (see tr_frag): lane 16 G + 4 j + q
+  // points at row 8 h + 4 (G / 2) + j, columns 32 db + 16 (G % 2) + 4 q .. +4
+  // (rows of a 16-row step relative to its first row).
+  const int G = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int row = 8 * h + 4 * (G >> 1) + j, col = 32 * db + 16 * (G & 1) + 4 * q;
+      o.ntr[h][db] = row * D + (((col >> 3) ^ swz<NCR>(row)) << 3) + (col & 7);
+    }
   return o;
+}
+
+// MFMA A operand T^T[m = column][k = row] of rows 16 s .. 16 s + 15 and
+// columns 32 db .. 32 db + 31 of a natural fp16 tile T (D columns), read
+// across the rows.  Within each group of 16 lanes the transposed read
+// gives lane i, element e, the (i % 4)-th value at the address of lane
+// 4 e + i / 4; with the addresses of lane_offsets, lane l receives column
+// 32 db + l % 32 of rows 16 s + 8 h + 4 (l / 32) + e, e = 0..3, for the two
+// halves h.  That is the row order in which an MFMA C tile hands its rows
+// over as a B operand (device.h), so no row permutation is stored.
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_tr;
+typedef __attribute__((address_space(3))) fp16x4_tr lds_fp16x4_tr;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ f16x8 tr_frag(const _Float16* step, const LaneOff<D>& o, int db) {
+  const fp16x4_tr lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_tr*)(lds_void*)(step + o.ntr[0][db]));
+  const fp16x4_tr hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_tr*)(lds_void*)(step + o.ntr[1][db]));
+  return __builtin_shufflevector(__builtin_bit_cast(f16x4, lo), __builtin_bit_cast(f16x4, hi), 0, 1, 2, 3, 4, 5,
+                                 6, 7);
 }
 
 // acc += A B with the accumulator held in AGPRs for the whole walk.  The
