@@ -162,8 +162,8 @@ struct FwdWs {
   _Float16* vt;
 };
 struct BwdWs {
-  uint16_t *kn, *vn;
-  _Float16* kt;
+  _Float16* kh;
+  uint16_t* vn;
   uint16_t *qn, *don;
   _Float16 *qh, *doh;
   float *lse2, *dc;
@@ -187,9 +187,8 @@ size_t carve_bwd(const Plan& P, char* base, BwdWs* w) {
   const size_t nq = (size_t)P.batch * P.hq * P.nqc * P.d;
   const size_t nr = (size_t)P.batch * P.hq * P.nqc;
   BwdWs t;
-  t.kn = cv.take<uint16_t>(nk);
+  t.kh = cv.take<_Float16>(nk);
   t.vn = cv.take<uint16_t>(nk);
-  t.kt = cv.take<_Float16>(nk);
   t.qn = cv.take<uint16_t>(nq);
   t.don = cv.take<uint16_t>(nq);
   t.qh = cv.take<_Float16>(nq);
@@ -449,16 +448,15 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   pk.v_clean = targ(v_clean);
   pk.k_corr = targ(k_corr);
   pk.v_corr = targ(v_corr);
-  pk.kn = ws.kn;
+  pk.kh = ws.kh;
   pk.vn = ws.vn;
-  pk.kt = ws.kt;
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kn, ws.vn,
+  DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kh, ws.vn,
               dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc};
   e = timed(K_DKDV, s, [&] { return launch_dkdv(P, ka, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DqArgs qa{ws.qn, ws.don, ws.lse2, ws.dc, ws.kn, ws.vn, ws.kt, dq_acc};
+  DqArgs qa{ws.qh, ws.don, ws.lse2, ws.dc, ws.kh, ws.vn, dq_acc};
   return hip_status(timed(K_DQ, s, [&] { return launch_dq(P, qa, s); }));
 }
 

@@ -28,9 +28,11 @@ namespace {
 //   S^T = K Q^T,  P^T = exp(S^T - LSE) (masked),  dP^T = V dO^T,
 //   dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T,
 // reading each K, V and K^T fragment from LDS once for both row blocks.
-// K and V (natural bf16) go from global memory straight into LDS
-// (global_load_lds), double buffered; K^T (fp16) is single buffered and
-// copied after the tile's last product has read it.
+// K (fp16 rows) and V (bf16 rows) go from global memory straight into LDS
+// (global_load_lds), double buffered; K^T fragments are read across the
+// rows of the staged K tile with the transposing LDS read.  S^T and dQ^T
+// run as fp16 products (Q, K converted exactly by the packing), dP^T in
+// bf16.
 constexpr int kDqWaves = 2;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRows = kBQ / kDqWaves;  // query rows per wave
@@ -40,9 +42,8 @@ static_assert(kBK == kTileRows, "key tiles are staged as 64-row tiles");
 template <int D>
 struct __attribute__((aligned(16))) DqSmem {
   static constexpr int TILE = kBK * D;  // elements per staged tile
-  uint16_t k[2][TILE];                  // natural bf16 [key][d]
-  uint16_t v[2][TILE];
-  _Float16 kt[TILE];                    // transposed fp16 [d][key], perm16 keys
+  _Float16 k[2][TILE];                  // fp16 [key][d]
+  uint16_t v[2][TILE];                  // bf16 [key][d]
 };
 
 template <int D>
@@ -50,7 +51,7 @@ constexpr int kDqPer = kBK * D / 512 / kDqWaves;  // 1 KB blocks per wave per ti
 
 template <int D>
 __device__ __forceinline__ int64_t dq_tile_base(const Plan& P, int b, int g, int32_t c) {
-  return uniform64(((int64_t)(b * P.hkv + g) * P.nkc + c) * D);  // natural and transposed alike
+  return uniform64(((int64_t)(b * P.hkv + g) * P.nkc + c) * D);
 }
 
 // Copies of key tile c: K and V into buffer B.
@@ -62,20 +63,8 @@ __device__ __forceinline__ void dq_stage_kv(const DqArgs& A, const Plan& P, int 
   for (int j = 0; j < kDqPer<D>; ++j) {
     const int blk = (wave + kDqWaves * j) * 512;
     const int64_t e = base + (int64_t)j * kDqWaves * 512;
-    copy16(A.kn + e, o.dn[j & 1], &sm.k[B][blk]);
+    copy16(A.kh + e, o.dn[j & 1], &sm.k[B][blk]);
     copy16(A.vn + e, o.dn[j & 1], &sm.v[B][blk]);
-  }
-}
-// Copies of key tile c: K^T.
-template <int D>
-__device__ __forceinline__ void dq_stage_kt(const DqArgs& A, const Plan& P, int b, int g, int32_t c, int wave,
-                                            const LaneOff<D>& o, DqSmem<D>& sm) {
-  const int64_t base = dq_tile_base<D>(P, b, g, c);
-#pragma unroll
-  for (int j = 0; j < kDqPer<D>; ++j) {
-    const int blk = (wave + kDqWaves * j) * 512;
-    const int64_t e = base + (int64_t)j * kDqWaves * 512;
-    copy16(A.kt + e, o.dt, &sm.kt[blk]);
   }
 }
 
@@ -83,27 +72,27 @@ __device__ __forceinline__ void dq_stage_kt(const DqArgs& A, const Plan& P, int 
 // B operands), for both key and row blocks; each fragment (ks, kb) is read
 // once and feeds both row blocks.
 template <int D>
-__device__ __forceinline__ void dq_products(const uint16_t* tile, int ql, const bf16x8 (&rows)[2][D / 16],
+__device__ __forceinline__ void dq_products(const _Float16* tile, int ql, const f16x8 (&rows)[2][D / 16],
                                             const LaneOff<D>& o, f32x16 (&acc)[2][2]) {
   constexpr int NF = 2 * (D / 16);
-  const uint16_t* tb = tile + ql * D;
-  bf16x8 fr[NF];
+  const _Float16* tb = tile + ql * D;
+  f16x8 fr[NF];
 #pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     if (f + kAhead < NF) {
       const int h = f + kAhead;
-      fr[h] = ld16<bf16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
+      fr[h] = ld16<f16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
     }
     const int kb = f & 1, ks = f >> 1;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       if (ks == 0)
-        acc[rb][kb] = mfma_bf16_bagpr0(fr[f], rows[rb][ks]);
+        acc[rb][kb] = mfma_f16_bagpr0(fr[f], rows[rb][ks]);
       else
-        mfma_bf16_bagpr(acc[rb][kb], fr[f], rows[rb][ks]);
+        mfma_f16_bagpr(acc[rb][kb], fr[f], rows[rb][ks]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -146,15 +135,14 @@ __device__ __forceinline__ void dq_ds_piece(int q, int kb, int ss, const f32x16 
   }
 }
 
-// One key tile of the wave's walk (buffers B for K, V; K^T single).  The
-// vector work of each stage runs between the matrix products of the next:
+// One key tile of the wave's walk (buffers B).  The vector work of each stage runs between the matrix products of the next:
 // the exponentials between the dP^T products, each dS^T chunk between the
 // dQ^T products of the previous chunk.
 template <int D>
 __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t c, const DqRows& rw, float c2,
-                                        int ql, int hh, const bf16x8 (&qreg)[2][D / 16],
+                                        int ql, int hh, const f16x8 (&qreg)[2][D / 16],
                                         const bf16x8 (&doreg)[2][D / 16], const LaneOff<D>& o,
-                                        f32x16 (&dqacc)[2][D / 32], int nkv) {
+                                        f32x16 (&dqacc)[2][D / 32]) {
   constexpr int NF = 2 * (D / 16);  // K or V fragments (ks, kb)
   // S^T
   f32x16 sc[2][2];
@@ -205,28 +193,22 @@ __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t
       }
     }
   }
-  mfma_settle();
-  dq_ds_chunk(0, 0, pc, rw.dval, pf);
-  // K^T of this tile has landed for every wave
-  if (nkv > 0)
-    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * kDqPer<D>) & 15) | (((2 * kDqPer<D>) >> 4) << 14));
-  else
-    wait_copies();
-  __syncthreads();
-  mfma_settle();
   // dQ^T += K^T dS^T; fragment f = (s, db) feeds both row blocks, chunk s + 1
   // of dS^T is formed during group s
   constexpr int NDB = D / 32, NT = (kBK / 16) * NDB;
-  const _Float16* tb = sm.kt + ql * kBK;
+  const _Float16* kb16 = sm.k[B];
   f16x8 fr[NT];
 #pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBK + o.tr[f / NDB]);
+  for (int f = 0; f < kAhead; ++f) fr[f] = tr_frag<D>(kb16 + (f / NDB) * 16 * D, o, f % NDB);
+  mfma_settle();
+  dq_ds_chunk(0, 0, pc, rw.dval, pf);
+  mfma_settle_short();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int f = 0; f < NT; ++f) {
     if (f + kAhead < NT) {
       const int h = f + kAhead;
-      fr[h] = ld16<f16x8>(tb + (h % NDB) * 32 * kBK + o.tr[h / NDB]);
+      fr[h] = tr_frag<D>(kb16 + (h / NDB) * 16 * D, o, h % NDB);
     }
     const int sk = f / NDB, db = f % NDB;
     if (db == 0 && sk > 0) mfma_settle_short();
@@ -255,7 +237,8 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
   const int64_t hb = (int64_t)(b * P.hq + h);
 
   // Q and dO of this lane's two rows (B operands, kept in AGPRs)
-  bf16x8 qreg[2][D / 16], doreg[2][D / 16];
+  f16x8 qreg[2][D / 16];
+  bf16x8 doreg[2][D / 16];
   DqRows rw;
   RowBounds rbd[2];
 #pragma unroll
@@ -264,7 +247,7 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
     const int64_t cr = hb * P.nqc + (int64_t)tile * kBQ + rq;  // compact (zero-padded) row
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      qreg[rb][ks] = ld16<bf16x8>(A.qn + cr * D + ks * 16 + hh * 8);
+      qreg[rb][ks] = ld16<f16x8>(A.qh + cr * D + ks * 16 + hh * 8);
       doreg[rb][ks] = ld16<bf16x8>(A.don + cr * D + ks * 16 + hh * 8);
       keep_in_agpr(qreg[rb][ks]);
       keep_in_agpr(doreg[rb][ks]);
@@ -288,7 +271,6 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
       bool fu;
       keywalk_at(w, 0, &c, &ri, &fu);
       dq_stage_kv<D>(A, P, b, g, c, wave, o, sm, 0);
-      dq_stage_kt<D>(A, P, b, g, c, wave, o, sm);
     }
     wait_copies();
     __syncthreads();
@@ -297,10 +279,8 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
       int32_t c, ri;
       bool full;
       keywalk_at(w, t, &c, &ri, &full);
-      const bool more = t + 1 < w.total;
-      int32_t cn = c;
-      if (more) {
-        int32_t rn;
+      if (t + 1 < w.total) {
+        int32_t cn, rn;
         bool fn;
         keywalk_at(w, t + 1, &cn, &rn, &fn);
         dq_stage_kv<D>(A, P, b, g, cn, wave, o, sm, B ^ 1);
@@ -309,10 +289,9 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) compact_range(P.k[ri], rbd[rb], clean, &rw.vlo[rb], &rw.vhi[rb]);
       }
-      dq_step<D>(sm, B, full, c, rw, c2, ql, hh, qreg, doreg, o, dqacc, more ? 1 : 0);
+      dq_step<D>(sm, B, full, c, rw, c2, ql, hh, qreg, doreg, o, dqacc);
       wait_copies();
-      __syncthreads();  // the next tile's K, V have landed; this tile's K^T reads are done
-      if (more) dq_stage_kt<D>(A, P, b, g, cn, wave, o, sm);
+      __syncthreads();  // the next tile's K, V have landed; this tile's reads are done
     }
   }
   agpr_settle();

@@ -26,7 +26,7 @@
 // XOR-swizzled by row.  S and dP read the tiles along their rows; the
 // contractions over rows (dV, dK) read the same tiles across their rows
 // with the transposing LDS read, so each operand is staged once.  All
-// products run in fp16 (K and V are converted once on load; Q and dO come
+// products run in fp16 (V is converted once on load; Q, dO and K come
 // converted): the values are those of the bf16 inputs.
 // The walk runs back to front by position (all heads of the group at each
 // position): the last rows are seen by every key tile, so the workgroups
@@ -305,13 +305,17 @@ __device__ __forceinline__ void dkdv_role(const Plan& P, const DkdvArgs& A, Dkdv
                                           int32_t nseg, int32_t total, const LaneOff<D>& o) {
   f16x8 kvreg[kKB][D / 16];
   {
-    const uint16_t* src = S_WAVE ? A.kn : A.vn;
     const int64_t nb = ((int64_t)(b * P.hkv + g) * P.nkc + c + kw * kKW + ql) * D + hh * 8;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        kvreg[kb][ks] = bf16x8_to_f16x8(ld16<u32x4>(src + nb + kb * 32 * D + ks * 16));
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int64_t e = nb + kb * 32 * D + ks * 16;
+        if constexpr (S_WAVE)
+          kvreg[kb][ks] = ld16<f16x8>(A.kh + e);
+        else
+          kvreg[kb][ks] = bf16x8_to_f16x8(ld16<u32x4>(A.vn + e));
+      }
   }
   f32x16 acc[D / 32][kKB];  // dV^T (S-wave) or dK^T (P-wave)
 #pragma unroll

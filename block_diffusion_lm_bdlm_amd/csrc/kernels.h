@@ -16,13 +16,13 @@ struct TensorArg {
 // ---------------------------------------------------------------- packing
 // Compact key space: the call's key segments back to back, each starting at
 // a multiple of kAlign, zero padded.  Natural layouts are [batch][hkv][nkc][d]
-// bf16; transposed ones fp16 [batch][hkv][nkc/64][d][64] (tiles of 64 rows,
-// each contiguous) with perm16 groups.
+// (bf16, or fp16 for kh); transposed ones fp16 [batch][hkv][nkc/64][d][64]
+// (tiles of 64 rows, each contiguous) with perm16 groups.
 struct PackKArgs {
   TensorArg k_clean, v_clean, k_corr, v_corr;  // bf16
   uint16_t* kn;   // natural K (nullable)
   uint16_t* vn;   // natural V (nullable)
-  _Float16* kt;   // transposed K (nullable)
+  _Float16* kh;   // natural K in fp16 (nullable)
   _Float16* vt;   // transposed V (nullable)
 };
 
@@ -67,13 +67,12 @@ struct DeltaArgs {
 };
 
 struct DqArgs {
-  const uint16_t* qn;  // compact query side
+  const _Float16* qh;  // compact query side (Q fp16, dO bf16)
   const uint16_t* don;
   const float* lse2;
   const float* dc;
-  const uint16_t* kn;  // compact key side
+  const _Float16* kh;  // compact key side (K fp16, V bf16)
   const uint16_t* vn;
-  const _Float16* kt;
   float* dq;  // [batch][R][hq][d], +=
 };
 
@@ -83,7 +82,7 @@ struct DkdvArgs {
   const float* lse2;
   const float* dc;
   const int32_t* vis;
-  const uint16_t* kn;
+  const _Float16* kh;
   const uint16_t* vn;
   float* dk_clean;  // [batch][L][hkv][d], +=
   float* dv_clean;

@@ -2,8 +2,8 @@
 //
 //  pack_k: gathers the call's key rows (clean token ranges, then the share's
 //          packed corrupted rows) into one compact, zero-padded key space;
-//          writes natural bf16 K/V and fp16 K^T/V^T.  The transposed copies
-//          are tiled: each tile of 64 rows is one contiguous [d][64] block
+//          writes the layouts its consumer asks for: natural bf16 K/V,
+//          natural fp16 K, transposed fp16 V^T.  The transposed copy is tiled: each tile of 64 rows is one contiguous [d][64] block
 //          (so a consumer's tile is a single 16 KB read), and every aligned
 //          group of 16 rows is in perm16 order, the order in which an MFMA C
 //          tile delivers its rows as a B operand.
@@ -26,8 +26,7 @@ static_assert(kPT == kBK, "consumers read whole transposed key tiles");
 
 template <int D>
 struct __attribute__((aligned(16))) PackSmem {
-  uint16_t a[kPT][D + 8];  // bf16 rows (16-byte aligned)
-  uint16_t b[kPT][D + 8];
+  uint16_t b[kPT][D + 8];  // bf16 rows of V (16-byte aligned)
 };
 
 __device__ inline _Float16 bf16_to_f16(uint16_t u) { return (_Float16)bf16_to_f32(u); }
@@ -75,13 +74,14 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
     const int64_t nat = ((int64_t)(b * P.hkv + g) * P.nkc + cc) * D + dc;
     if (A.kn) *reinterpret_cast<u32x4*>(A.kn + nat) = kv;
     if (A.vn) *reinterpret_cast<u32x4*>(A.vn + nat) = vv;
-    *reinterpret_cast<u32x4*>(&sm.a[r][dc]) = kv;
+    if (A.kh) *reinterpret_cast<f16x8*>(A.kh + nat) = bf16x8_to_f16x8(kv);
     *reinterpret_cast<u32x4*>(&sm.b[r][dc]) = vv;
   }
-  __syncthreads();
-  const int64_t tb = (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // tile c / kPT
-  if (A.kt) store_transposed<D>(sm.a, A.kt + tb, tid);
-  if (A.vt) store_transposed<D>(sm.b, A.vt + tb, tid);
+  if (A.vt) {
+    __syncthreads();
+    const int64_t tb = (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // tile c / kPT
+    store_transposed<D>(sm.b, A.vt + tb, tid);
+  }
 }
 
 template <int D>
