@@ -98,9 +98,15 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
         keywalk_at(w, t + 1, &cn, &rn, &fn);
         fwd_stage<D>(A, P, b, g, cn, wave, o, sm, buf ^ 1);
       }
-      // S^T = K Q^T for two blocks of 32 keys
+      // S^T = K Q^T for two blocks of 32 keys.  The two waves sharing a SIMD
+      // belong to different workgroups; a wave raises its priority while it
+      // issues matrix products and drops it for the softmax, so the other
+      // wave's vector work fills the matrix core's shadow instead of
+      // competing with it.
       f32x16 sacc[2];
+      __builtin_amdgcn_s_setprio(2);
       scores_2kb<D>(sm.k[buf], ql, qreg, o, sacc);
+      __builtin_amdgcn_s_setprio(0);
       if (!full) {
         int32_t vlo, vhi;
         compact_range(P.k[ri], rb, clean, &vlo, &vhi);
@@ -139,6 +145,7 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       }
       m_run = m_new;
       // O^T += V^T P^T; fragment f = (s, db), s = 16-key step
+      __builtin_amdgcn_s_setprio(2);
       {
         constexpr int NDB = D / 32, NF = (kBK / 16) * NDB;
         const _Float16* tb = sm.vt[buf] + ql * kBK;
@@ -157,6 +164,7 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       wait_copies();
       __syncthreads();  // the next tile's copies have landed; this tile's reads are done
     }
