@@ -181,8 +181,9 @@ __device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7
 
 // Fragment reads kept in flight ahead of the products that consume them;
 // scheduling barriers pin this order (the compiler otherwise sinks each
-// read to its first use).
-constexpr int kAhead = 6;
+// read to its first use).  Measured at 2..10 on the 64K workload: 2-4 are
+// best (about 2% over 6); deeper queues only lengthen the LDS queue.
+constexpr int kAhead = 4;
 
 // C^T blocks of one staged natural tile: acc[kb] = tile[kb*32 .. +32][:]
 // times the lane's row held in registers (B operand), for the two 32-row
