@@ -21,7 +21,7 @@ BDATTN_MAX_RUNS = 8
 class Problem(C.Structure):
     _fields_ = [("batch", C.c_int32), ("L", C.c_int32), ("M", C.c_int32), ("hq", C.c_int32),
                 ("hkv", C.c_int32), ("d", C.c_int32), ("dtype", C.c_int32),
-                ("clean_mask", C.c_int32), ("scale", C.c_float)]
+                ("clean_mask", C.c_int32), ("scale", C.c_float), ("window", C.c_int32)]
 
 
 class Share(C.Structure):
@@ -86,8 +86,9 @@ def _check(status, what):
 
 
 # ------------------------------------------------------------------ builders
-def problem(batch, L, M, hq, hkv, d, dtype=BDATTN_BF16, clean_mask=BDATTN_CLEAN_BLOCK_CAUSAL, scale=0.0):
-    return Problem(batch, L, M, hq, hkv, d, dtype, clean_mask, scale)
+def problem(batch, L, M, hq, hkv, d, dtype=BDATTN_BF16, clean_mask=BDATTN_CLEAN_BLOCK_CAUSAL, scale=0.0,
+            window=0):
+    return Problem(batch, L, M, hq, hkv, d, dtype, clean_mask, scale, window)
 
 
 def share(blocks=(), clean=()):

@@ -25,6 +25,7 @@ bool problem_ok(const bdattn_problem* p) {
   if (p->clean_mask != BDATTN_CLEAN_BLOCK_CAUSAL && p->clean_mask != BDATTN_CLEAN_TOKEN_CAUSAL)
     return false;
   if (!std::isfinite(p->scale)) return false;
+  if (p->window < 0) return false;
   if ((int64_t)p->batch * p->hq > (1 << 20) || p->L > (1 << 29)) return false;
   return true;
 }
@@ -79,6 +80,7 @@ Plan make_plan(const bdattn_problem* p, const bdattn_share* s, const bdattn_kv* 
   P.d = p->d;
   P.G = p->hq / p->hkv;
   P.token_causal = p->clean_mask == BDATTN_CLEAN_TOKEN_CAUSAL;
+  P.window = p->window;
   P.scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt((float)p->d);
   P.scale_log2 = P.scale * 1.4426950408889634f;
   int32_t row = 0, tile = 0;

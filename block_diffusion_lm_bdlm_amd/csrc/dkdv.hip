@@ -272,7 +272,7 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
       const int32_t r0 = row_of(cur);
       bool full = false;
       if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= S.nrows)
-        full = row_bounds(P, S, r0).hi_clean >= kt1;
+        full = row_bounds(P, S, r0).hi_clean >= kt1 && row_bounds(P, S, r0 + kBQB - 1).lo_clean <= kt1 - kvalid;
       f16x8 pf[kRB][kKB][2];
       if (full)
         s_phase_a<D, true>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);

@@ -127,6 +127,7 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
       int32_t v[4] = {0, 0, 0, 0};
       if (rr < S.nrows) {
         const RowBounds rb = row_bounds(P, S, rr);
+        v[0] = rb.lo_clean;
         v[1] = rb.hi_clean;
         if (S.kind == KIND_CORR) {
           v[2] = rb.lo_loc;

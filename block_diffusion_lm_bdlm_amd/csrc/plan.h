@@ -9,7 +9,10 @@
 // and "CSBP：BP 管损坏块，CP 管干净上下文"): a corrupted query of block b sees
 // clean tokens < b*M and the corrupted tokens of block b; a clean query of
 // token t sees clean tokens < (t/M + 1)*M (block-causal) or <= t
-// (token-causal).
+// (token-causal).  With a sliding window W over the clean keys, a query at
+// token position t (the corrupted token at offset i of block b sits at
+// b*M + i) sees clean token j only if t - j < W.  Every row therefore sees
+// one interval of clean tokens, and both its ends grow with the row.
 //
 // Load balance ("CSBP 完全拆解", section "负载均衡：为什么要首尾块配对"): the
 // query tiles of each kind are paired early with late (tile t with tile
@@ -53,6 +56,7 @@ struct KSeg {
 
 struct Plan {
   int32_t batch, L, M, hq, hkv, d, G, token_causal;
+  int32_t window;         // clean-key sliding window in tokens (0 = none)
   float scale, scale_log2;
   int32_t R;              // share rows
   int32_t n_clean_rows;   // share clean rows (first in row order)
@@ -122,10 +126,17 @@ __host__ __device__ inline int32_t seg_of_tile(const Plan& P, int32_t t) {
 
 // Visible key interval(s) of one query row, in source-row coordinates.
 struct RowBounds {
-  int32_t hi_clean;  // clean tokens [0, hi_clean) are visible
+  int32_t lo_clean;  // clean tokens [lo_clean, hi_clean) are visible
+  int32_t hi_clean;
   int32_t lo_loc;    // packed corrupted rows [lo_loc, hi_loc) are visible
   int32_t hi_loc;
 };
+
+// Token position of row 0 of segment s (rows of a segment are consecutive
+// tokens: clean tokens, or the tokens of consecutive blocks).
+__host__ __device__ inline int64_t seg_token0(const Plan& P, const QSeg& s) {
+  return s.kind == KIND_CLEAN ? (int64_t)s.first : (int64_t)s.first * P.M;
+}
 
 __host__ __device__ inline RowBounds row_bounds(const Plan& P, const QSeg& s, int32_t r) {
   RowBounds rb;
@@ -139,6 +150,8 @@ __host__ __device__ inline RowBounds row_bounds(const Plan& P, const QSeg& s, in
     rb.lo_loc = s.src0 + r - r % P.M;
     rb.hi_loc = rb.lo_loc + P.M;
   }
+  const int64_t lo = P.window > 0 ? seg_token0(P, s) + r - P.window + 1 : 0;
+  rb.lo_clean = lo > 0 ? (int32_t)lo : 0;
   return rb;
 }
 
@@ -150,8 +163,9 @@ __host__ __device__ inline int32_t clampi(int32_t x, int32_t lo, int32_t hi) {
 __host__ __device__ inline void compact_range(const KSeg& ks, const RowBounds& rb, bool clean_row,
                                               int32_t* vlo, int32_t* vhi) {
   if (ks.kind == KIND_CLEAN) {
-    *vlo = ks.c0;
+    *vlo = ks.c0 + clampi(rb.lo_clean - ks.t0, 0, ks.len);
     *vhi = ks.c0 + clampi(rb.hi_clean - ks.t0, 0, ks.len);
+    if (*vhi < *vlo) *vhi = *vlo;
   } else if (clean_row) {
     *vlo = *vhi = ks.c0;
   } else {
@@ -232,7 +246,12 @@ __host__ __device__ inline int32_t first_seeing_row(const Plan& P, const QSeg& s
 // `k1` (exclusive end of the key tile).
 __host__ __device__ inline int32_t end_seeing_row(const Plan& P, const QSeg& s, int32_t kkind,
                                                   int32_t k1) {
-  if (kkind == KIND_CLEAN) return s.nrows;
+  if (kkind == KIND_CLEAN) {
+    if (P.window <= 0) return s.nrows;
+    // rows at token position >= k1 + W - 1 see only clean tokens >= k1
+    const int64_t r = (int64_t)k1 + P.window - 1 - seg_token0(P, s);
+    return (int32_t)(r < 0 ? 0 : (r > s.nrows ? s.nrows : r));
+  }
   if (s.kind == KIND_CLEAN) return 0;
   const int32_t pmax = ((k1 + P.M - 1) / P.M) * P.M;
   return clampi(pmax - s.src0, 0, s.nrows);

@@ -39,10 +39,11 @@ class WholeMask:
     dtype: int = B.BDATTN_BF16
     clean_mask: int = B.BDATTN_CLEAN_BLOCK_CAUSAL
     scale: float = 0.0
+    window: int = 0  # clean-key sliding window in tokens; 0 = none
 
     def __post_init__(self):
         self.prob = B.problem(self.batch, self.L, self.M, self.hq, self.hkv, self.d, self.dtype,
-                              self.clean_mask, self.scale)
+                              self.clean_mask, self.scale, self.window)
         self.share = B.share(range(self.L // self.M), [(0, self.L)])
         self.kv = B.kv([(0, self.L)], True)
 
@@ -99,10 +100,11 @@ class CsbpShare:
     clean_q: list = field(default_factory=list)
     shards: list = field(default_factory=list)  # list of lists of (lo, hi) clean key ranges
     scale: float = 0.0
+    window: int = 0  # clean-key sliding window in tokens; 0 = none
 
     def __post_init__(self):
         self.prob = B.problem(self.batch, self.L, self.M, self.hq, self.hkv, self.d, B.BDATTN_BF16,
-                              B.BDATTN_CLEAN_BLOCK_CAUSAL, self.scale)
+                              B.BDATTN_CLEAN_BLOCK_CAUSAL, self.scale, self.window)
         self.share = B.share(self.blocks, self.clean_q)
         self.kv_local = B.kv([], True)
         self.kv_shards = [B.kv(s, False) for s in self.shards]

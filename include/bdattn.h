@@ -94,12 +94,23 @@ typedef enum bdattn_clean_mask {
 /* Problem statement: L clean tokens, block size M (M divides L), hq query
  * heads sharing hkv key/value heads (query head h uses KV head
  * h / (hq/hkv)), head dimension d (64 or 128), input dtype, clean-copy
- * mask, logit scale (<= 0 selects 1/sqrt(d); [P1] CP attention equation). */
+ * mask, logit scale (<= 0 selects 1/sqrt(d); [P1] CP attention equation),
+ * and an optional sliding window over the clean keys.
+ *
+ * Sliding window ([P1] "实验数字：256K 上下文下的主结果" and [P3] "Under the
+ * hood", "Where does the time go?": most layers of one of the pages' models
+ * attend through a 1,024-token sliding window, and the sharded form then
+ * exchanges only the clean rows a rank's queries can see).  window = 0 means
+ * none.  Otherwise a query at token position t -- clean token t, or the
+ * corrupted token at offset i of block b, t = b*M + i -- sees clean key j
+ * only if t - j < window, in addition to the rules above.  The corrupted
+ * keys of the query's own block are not windowed. */
 typedef struct bdattn_problem {
   int32_t batch, L, M, hq, hkv, d;
   int32_t dtype;      /* bdattn_dtype of q, k, v, d_o */
   int32_t clean_mask; /* bdattn_clean_mask */
   float scale;
+  int32_t window;     /* clean-key sliding window in tokens; 0 = none */
 } bdattn_problem;
 
 /* Maximum number of runs of consecutive block ids in a share's block list. */

@@ -60,16 +60,26 @@ static inline int64_t koff(const orc_problem* p, int64_t b, int64_t j, int64_t g
  *  - Clean queries never read corrupted keys: corrupted K/V are read only by
  *    their own block (Turbo-dLLM page, "Method").
  */
+/*  - Sliding window (optional): "CSBP 完全拆解", section "实验数字：256K 上下
+ *    文下的主结果", and the Turbo-dLLM page, "Where does the time go?", name
+ *    a 1,024-token sliding window over the clean context for most layers of
+ *    one model without defining it further.  Read here on token distance: a
+ *    query at token position t (the clean token t, or the corrupted token
+ *    at offset i of block b, t = b*M + i) sees clean token j only if
+ *    t - j < window.  Corrupted keys of the query's own block are not
+ *    windowed.  window = 0: no window.
+ */
 int orc_visible(const orc_problem* p, int64_t i, int64_t j) {
   const int64_t L = p->L, M = p->M;
   if (i < L) {
     if (j >= L) return 0;
+    if (p->window > 0 && i - j >= p->window) return 0;
     if (p->token_causal) return j <= i;
     return j / M <= i / M;
   }
   {
-    const int64_t b = (i - L) / M;
-    if (j < L) return j / M < b;
+    const int64_t b = (i - L) / M, t = i - L;
+    if (j < L) return j / M < b && !(p->window > 0 && t - j >= p->window);
     return (j - L) / M == b;
   }
 }

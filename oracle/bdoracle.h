@@ -39,6 +39,7 @@ typedef struct orc_problem {
   int32_t token_causal; /* clean-copy mask: 0 block-causal, 1 token-causal */
   int32_t in_dtype;     /* ORC_F32 or ORC_BF16 */
   double scale;         /* logit scale, normally 1/sqrt(d) */
+  int32_t window;       /* clean-key sliding window in tokens; 0 = none (see orc_visible) */
 } orc_problem;
 
 /* Key subset of one call.  n_ranges < 0: every clean key; otherwise the

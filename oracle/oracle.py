@@ -22,7 +22,7 @@ class Problem(C.Structure):
     _fields_ = [("batch", C.c_int32), ("L", C.c_int32), ("M", C.c_int32),
                 ("hq", C.c_int32), ("hkv", C.c_int32), ("d", C.c_int32),
                 ("token_causal", C.c_int32), ("in_dtype", C.c_int32),
-                ("scale", C.c_double)]
+                ("scale", C.c_double), ("window", C.c_int32)]
 
 
 class Keys(C.Structure):
@@ -69,9 +69,9 @@ def num_threads():
     return lib().orc_num_threads()
 
 
-def problem(batch, L, M, hq, hkv, d, token_causal=False, bf16=False, scale=None):
+def problem(batch, L, M, hq, hkv, d, token_causal=False, bf16=False, scale=None, window=0):
     return Problem(batch, L, M, hq, hkv, d, int(bool(token_causal)), int(bool(bf16)),
-                   float(scale) if scale is not None else 1.0 / np.sqrt(d))
+                   float(scale) if scale is not None else 1.0 / np.sqrt(d), int(window))
 
 
 def keys(ranges=None, local=True):

@@ -119,6 +119,7 @@ def test_invalid_arguments_rejected_on_host():
         (B.problem(1, 1000, 16, 4, 2, 128), ok_s, ok_k),            # L % M != 0
         (B.problem(1, 1024, 16, 5, 2, 128), ok_s, ok_k),            # hq % hkv != 0
         (B.problem(0, 1024, 16, 4, 2, 128), ok_s, ok_k),            # batch 0
+        (B.problem(1, 1024, 16, 4, 2, 128, window=-1), ok_s, ok_k),  # negative window
         (ok_p, B.share([3, 2], []), ok_k),                          # unsorted blocks
         (ok_p, B.share([0, 0], []), ok_k),                          # repeated block
         (ok_p, B.share([64], []), ok_k),                            # block out of range

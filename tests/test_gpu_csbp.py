@@ -28,7 +28,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _rank(dev, L, M, hq, hkv, d, P, r, clean_queries, seed):
+def _rank(dev, L, M, hq, hkv, d, P, r, clean_queries, seed, window=0):
     from block_diffusion_lm_bdlm_amd import bdattn as B
     from block_diffusion_lm_bdlm_amd.runner import CsbpShare
     blocks = B.bdattn_assign_blocks(L // M, P, r).tolist()
@@ -39,7 +39,7 @@ def _rank(dev, L, M, hq, hkv, d, P, r, clean_queries, seed):
         k = B.bdattn_clean_shard(L, P, s)
         shards.append([(k.lo[0], k.hi[0]), (k.lo[1], k.hi[1])])
     t = csbp_inputs(seed, L, M, hq, hkv, d, blocks, clean_q, device=dev)
-    sh = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, shards)
+    sh = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, shards, window=window)
     o32, lse, obf = sh.fwd(t["q_clean"], t["q_corr"], t["k_clean"], t["v_clean"], t["k_corr"], t["v_corr"])
     grads = sh.bwd(t["q_clean"], t["q_corr"], t["k_clean"], t["v_clean"], t["k_corr"], t["v_corr"],
                    o32, lse, t["do"])
@@ -47,13 +47,15 @@ def _rank(dev, L, M, hq, hkv, d, P, r, clean_queries, seed):
     return blocks, clean_q, t, o32, lse, obf, grads
 
 
-@pytest.mark.parametrize("L,M,hq,hkv,d,P", [(1024, 16, 4, 2, 128, 4), (768, 32, 2, 1, 64, 3),
-                                            (512, 8, 4, 4, 128, 2)])
-def test_virtual_ranks(dev, orc, L, M, hq, hkv, d, P):
+@pytest.mark.parametrize("L,M,hq,hkv,d,P,W", [(1024, 16, 4, 2, 128, 4, 0), (768, 32, 2, 1, 64, 3, 0),
+                                              (512, 8, 4, 4, 128, 2, 0), (1024, 16, 4, 2, 128, 4, 200)])
+def test_virtual_ranks(dev, orc, L, M, hq, hkv, d, P, W):
+    """W > 0: the same under a clean-key sliding window of W tokens (most
+    shards are then outside most rows' windows and contribute the identity)."""
     seed = 100 + L
     # every rank uses the same clean K/V (shared context) and its own corrupted / query rows:
     # build the oracle's doubled input from all ranks' pieces
-    ranks = [_rank(dev, L, M, hq, hkv, d, P, r, True, seed) for r in range(P)]
+    ranks = [_rank(dev, L, M, hq, hkv, d, P, r, True, seed, window=W) for r in range(P)]
     qh = np.zeros((1, 2 * L, hq, d), np.uint16)
     doh = np.zeros_like(qh)
     kh = np.zeros((1, 2 * L, hkv, d), np.uint16)
@@ -67,7 +69,7 @@ def test_virtual_ranks(dev, orc, L, M, hq, hkv, d, P):
         kx = pos[len(pos) - len(blocks) * M:]
         kh[0, kx] = k_[0, kx]
         vh[0, kx] = v_[0, kx]
-    p = orc.problem(1, L, M, hq, hkv, d, bf16=True)
+    p = orc.problem(1, L, M, hq, hkv, d, bf16=True, window=W)
     o_ref, lse_ref = orc.fwd(p, orc.keys(), qh, kh, vh)
     dq_ref, dk_ref, dv_ref = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), qh, kh, vh, doh)
     dkc = np.zeros((L, hkv, d))

@@ -36,13 +36,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _run(dev, shape, dtype, bwd=True, seed=1):
+def _run(dev, shape, dtype, bwd=True, seed=1, window=0):
     from block_diffusion_lm_bdlm_amd import bdattn as B
     from block_diffusion_lm_bdlm_amd.runner import WholeMask
     batch, L, M, hq, hkv, d, tc = shape
     q, k, v, do = doubled_inputs(seed, batch, L, hq, hkv, d, dtype=dtype, device=dev)
     wm = WholeMask(batch, L, M, hq, hkv, d, B.BDATTN_F32 if dtype == torch.float32 else B.BDATTN_BF16,
-                   B.BDATTN_CLEAN_TOKEN_CAUSAL if tc else B.BDATTN_CLEAN_BLOCK_CAUSAL)
+                   B.BDATTN_CLEAN_TOKEN_CAUSAL if tc else B.BDATTN_CLEAN_BLOCK_CAUSAL, window=window)
     o32, lse = wm.fwd(q, k, v, o_dtype=torch.float32)
     out = {"o": o32, "lse": lse}
     if bwd:
@@ -131,3 +131,41 @@ def test_large_blocks(dev, orc, shape):
     assert rel_l2(got["dq"], dq) <= TOL_GRAD
     assert rel_l2(got["dk"], dk) <= TOL_GRAD
     assert rel_l2(got["dv"], dv) <= TOL_GRAD
+
+
+# Sliding window over the clean keys (pages: most layers of one of the
+# pages' models attend through a 1,024-token window): windows narrower than
+# a block, not aligned to any tile, wider than everything, token-causal.
+WSHAPES = [
+    # batch, L, M, hq, hkv, d, token_causal, window
+    (1, 512, 32, 4, 2, 128, False, 100),
+    (2, 384, 16, 2, 1, 64, False, 8),
+    (1, 640, 32, 2, 1, 128, True, 130),
+    (1, 256, 16, 2, 2, 128, False, 1),
+    (1, 320, 32, 2, 1, 128, False, 1000),
+    (1, 2048, 64, 2, 1, 128, False, 1024),
+]
+
+
+@pytest.mark.parametrize("shape", WSHAPES, ids=[str(s) for s in WSHAPES])
+def test_window_bf16(dev, orc, shape):
+    batch, L, M, hq, hkv, d, tc, W = shape
+    (q, k, v, do), got = _run(dev, shape[:7], torch.bfloat16, seed=4, window=W)
+    p = orc.problem(batch, L, M, hq, hkv, d, token_causal=tc, bf16=True, window=W)
+    hq_, hk_, hv_, hdo = (host_bits(x) for x in (q, k, v, do))
+    o, lse = orc.fwd(p, orc.keys(), hq_, hk_, hv_)
+    assert max_abs(got["o"], o) <= TOL_O
+    assert max_abs(got["lse"], lse) <= TOL_LSE
+    dq, dk, dv = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), hq_, hk_, hv_, hdo)
+    assert rel_l2(got["dq"], dq) <= TOL_GRAD
+    assert rel_l2(got["dk"], dk) <= TOL_GRAD
+    assert rel_l2(got["dv"], dv) <= TOL_GRAD
+
+
+def test_window_f32(dev, orc):
+    shape = (1, 256, 16, 2, 1, 64, False)
+    (q, k, v, _), got = _run(dev, shape, torch.float32, bwd=False, seed=6, window=37)
+    p = orc.problem(1, 256, 16, 2, 1, 64, window=37)
+    o, lse = orc.fwd(p, orc.keys(), *(host_bits(x) for x in (q, k, v)))
+    assert max_abs(got["o"], o) <= TOL_F32
+    assert max_abs(got["lse"], lse) <= TOL_F32

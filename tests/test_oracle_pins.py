@@ -22,11 +22,21 @@ GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 # ---------------------------------------------------------------- helpers
-def dense_mask(L, M, token_causal=False):
+def window_band(L, W):
+    """Clean-key sliding window as a band: entry (t, j) kept when j >= t - W + 1
+    (np.triu with offset -(W - 1)); W = 0 keeps everything."""
+    if W <= 0:
+        return np.ones((L, L), dtype=bool)
+    return np.triu(np.ones((L, L), dtype=bool), -(W - 1))
+
+
+def dense_mask(L, M, token_causal=False, window=0):
     """Doubled-input mask from block products: clean rows over the clean copy
     (block lower-triangular of ones, or token lower-triangular), corrupted
     block b over clean blocks < b (strict block lower-triangular) and its own
-    corrupted block (block diagonal)."""
+    corrupted block (block diagonal).  A window cuts both clean-key blocks
+    with the same band (the corrupted copy's rows are the same token
+    positions as the clean copy's)."""
     B = L // M
     E = np.ones((M, M), dtype=bool)
     if token_causal:
@@ -34,6 +44,8 @@ def dense_mask(L, M, token_causal=False):
     else:
         cc = np.kron(np.tril(np.ones((B, B), dtype=bool)), E)
     xc = np.kron(np.tril(np.ones((B, B), dtype=bool), -1), E)
+    band = window_band(L, window)
+    cc, xc = cc & band, xc & band
     xx = np.kron(np.eye(B, dtype=bool), E)
     top = np.concatenate([cc, np.zeros((L, L), dtype=bool)], 1)
     bot = np.concatenate([xc, xx], 1)
@@ -400,6 +412,128 @@ def test_finite_differences(orc, tc):
             bp = dict(base, **{which: plus})
             bm = dict(base, **{which: minus})
             fd = (loss(bp["q"], bp["k"], bp["v"]) - loss(bm["q"], bm["k"], bm["v"])) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(grad[idx])), (which, idx, fd, grad[idx])
+
+
+# ---------------------------------------------------------------- sliding window
+WINDOWS = [(16, 4, 1), (16, 4, 3), (16, 4, 4), (16, 4, 7), (24, 4, 9), (32, 8, 5), (16, 1, 4),
+           (16, 16, 5), (16, 4, 40)]
+
+
+@pytest.mark.parametrize("L,M,W", WINDOWS)
+@pytest.mark.parametrize("token_causal", [False, True])
+def test_window_mask_counts_closed_form(orc, L, M, W, token_causal):
+    """Per-row visible counts under a clean-key window of W tokens, derived by
+    hand: clean block-causal row t sees (t//M + 1) M - max(0, t - W + 1),
+    clean token-causal row t sees min(t + 1, W), corrupted row (block b,
+    offset i) sees M + max(0, min(b M, W - 1 - i))."""
+    p = orc.problem(1, L, M, 1, 1, 4, token_causal=token_causal, window=W)
+    vis = np.array([[orc.visible(p, i, j) for j in range(2 * L)] for i in range(2 * L)], dtype=bool)
+    assert (vis == dense_mask(L, M, token_causal, W)).all()
+    for t in range(L):
+        n = min(t + 1, W) if token_causal else (t // M + 1) * M - max(0, t - W + 1)
+        assert vis[t].sum() == n
+        b, i = divmod(t, M)
+        assert vis[L + t].sum() == M + max(0, min(b * M, W - 1 - i))
+
+
+WSHAPES = [
+    # batch, L, M, hq, hkv, d, token_causal, window
+    (1, 16, 4, 2, 1, 8, False, 6),
+    (2, 16, 4, 4, 2, 4, True, 5),
+    (1, 24, 3, 2, 2, 6, False, 2),
+    (1, 16, 8, 2, 1, 4, False, 9),
+]
+
+
+@pytest.mark.parametrize("shape", WSHAPES)
+def test_window_fwd_bwd_match_dense(orc, shape):
+    batch, L, M, hq, hkv, d, tc, W = shape
+    q, k, v, do = rand_inputs(batch, L, hq, hkv, d, seed=51 + W)
+    p = orc.problem(batch, L, M, hq, hkv, d, token_causal=tc, window=W)
+    o, lse = orc.fwd(p, orc.keys(), q, k, v)
+    dq, dk, dv = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), q, k, v, do)
+    tq, tk, tv = (as_f64(x).requires_grad_(True) for x in (q, k, v))
+    ro, rlse = dense_attention(tq, tk, tv, dense_mask(L, M, tc, W), p.scale)
+    np.testing.assert_allclose(o, ro.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse.detach().numpy(), rtol=0, atol=1e-12)
+    (ro * as_f64(do)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_window_sdpa_special_case(orc):
+    """M = 1, token-causal: the clean copy is standard causal sliding-window
+    attention; torch's SDPA with a banded causal mask (tril, then triu)."""
+    F = torch.nn.functional
+    batch, L, hq, d, W = 2, 16, 2, 8, 5
+    q, k, v, _ = rand_inputs(batch, L, hq, hq, d, seed=57)
+    tq, tk, tv = (as_f64(x).transpose(1, 2) for x in (q, k, v))
+    p = orc.problem(batch, L, 1, hq, hq, d, token_causal=True, window=W)
+    o, _ = orc.fwd(p, orc.keys(), q, k, v)
+    band = torch.ones(L, L, dtype=torch.bool).tril().triu(-(W - 1))
+    ref = F.scaled_dot_product_attention(tq[:, :, :L], tk[:, :, :L], tv[:, :, :L], attn_mask=band)
+    np.testing.assert_allclose(o[:, :L], ref.transpose(1, 2).numpy(), atol=1e-12)
+
+
+def test_window_wide_is_none(orc):
+    """A window at least as long as the sequence changes nothing, bit for bit."""
+    batch, L, M, hq, hkv, d = 1, 16, 4, 2, 1, 8
+    q, k, v, do = rand_inputs(batch, L, hq, hkv, d, seed=59)
+    p0 = orc.problem(batch, L, M, hq, hkv, d)
+    pw = orc.problem(batch, L, M, hq, hkv, d, window=L)
+    for a, b in zip(orc.fwd(p0, orc.keys(), q, k, v), orc.fwd(pw, orc.keys(), q, k, v)):
+        assert np.array_equal(a, b)
+    for a, b in zip(orc.bwd(p0, orc.share(), orc.keys(), orc.keys(), q, k, v, do),
+                    orc.bwd(pw, orc.share(), orc.keys(), orc.keys(), q, k, v, do)):
+        assert np.array_equal(a, b)
+
+
+def test_window_csbp_identities(orc):
+    """Under a window the LSE merge over zigzag shards still equals the
+    unsharded forward, and the per-shard backward still sums to the full
+    gradient (shards far outside a row's window contribute the identity)."""
+    batch, L, M, hq, hkv, d, W, P = 1, 32, 4, 4, 2, 4, 7, 4
+    q, k, v, do = rand_inputs(batch, L, hq, hkv, d, seed=61)
+    p = orc.problem(batch, L, M, hq, hkv, d, window=W)
+    o_ref, l_ref = orc.fwd(p, orc.keys(), q, k, v)
+    o_acc, l_acc = orc.fwd(p, orc.keys([], local=True), q, k, v)
+    calls = [orc.keys(orc.clean_shard(L, P, s), local=False) for s in range(P)]
+    for kg in calls:
+        o_s, l_s = orc.fwd(p, kg, q, k, v)
+        o_acc, l_acc = orc.merge(o_acc, l_acc, o_s, l_s)
+    np.testing.assert_allclose(o_acc, o_ref, atol=1e-12)
+    np.testing.assert_allclose(l_acc, l_ref, atol=1e-12)
+    full = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), q, k, v, do)
+    acc = [np.zeros_like(x) for x in full]
+    for kg in [orc.keys([], local=True)] + calls:
+        for a, x in zip(acc, orc.bwd(p, orc.share(), orc.keys(), kg, q, k, v, do)):
+            a += x
+    for a, x in zip(acc, full):
+        np.testing.assert_allclose(a, x, atol=1e-12)
+
+
+def test_window_finite_differences(orc):
+    batch, L, M, hq, hkv, d, W = 1, 16, 4, 2, 1, 4, 6
+    q, k, v, do = rand_inputs(batch, L, hq, hkv, d, seed=67)
+    p = orc.problem(batch, L, M, hq, hkv, d, window=W)
+    dq, dk, dv = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), q, k, v, do)
+    eps = 2.0 ** -14
+    do64 = do.astype(np.float64)
+    g = np.random.default_rng(71)
+    for which, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(4):
+            base = {"q": q, "k": k, "v": v}
+            idx = tuple(int(g.integers(0, s)) for s in base[which].shape)
+            vals = []
+            for sgn in (1, -1):
+                a = base[which].copy()
+                a[idx] += sgn * eps
+                bb = dict(base, **{which: a})
+                o, _ = orc.fwd(p, orc.keys(), bb["q"], bb["k"], bb["v"])
+                vals.append(float((o * do64).sum()))
+            fd = (vals[0] - vals[1]) / (2 * eps)
             assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(grad[idx])), (which, idx, fd, grad[idx])
 
 
