@@ -69,8 +69,24 @@ def calibrate_copy(nbytes):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
-def visible_pairs(L, M):
-    return L * (L + M)
+def visible_pairs(L, M, window=0, token_causal=False):
+    """Visible (query, key) pairs per head of the whole mask.  Without a
+    window, L (L + M) for the block-causal clean copy.  With a clean-key
+    window W, per token position t (block b = t // M, offset i = t % M):
+    the clean row sees (b + 1) M - max(0, t - W + 1) keys (min(t + 1, W)
+    token-causal) and the corrupted row M + max(0, min(b M, W - 1 - i))."""
+    if window <= 0 and not token_causal:
+        return L * (L + M)
+    t = np.arange(L, dtype=np.int64)
+    b, i = t // M, t % M
+    if window <= 0:
+        return int((t + 1).sum() + ((b + 1) * M).sum())
+    if token_causal:
+        clean = np.minimum(t + 1, window)
+    else:
+        clean = (b + 1) * M - np.maximum(0, t - window + 1)
+    corr = M + np.maximum(0, np.minimum(b * M, window - 1 - i))
+    return int(clean.sum() + corr.sum())
 
 
 def kernel_flops(name, pairs, hq, batch, d):
@@ -150,17 +166,21 @@ def report_all(reps=3):
         return e0.elapsed_time(e1) / reps
 
     rows = []
-    whole = [("fp32_L1K_M16_h4_d64_fwd", 0, (1, 1024, 16, 4, 4, 64), torch.float32, 1.0, False),
-             ("bf16_L8K_M32_b2_h16kv8", 1, (2, 8192, 32, 16, 8, 128), torch.bfloat16, 128 ** -0.5, True),
-             ("bf16_L64K_M32_h40kv8", 2, (1, 65536, 32, 40, 8, 128), torch.bfloat16, 1.0, True)]
-    for name, idx, (batch, L, M, hq, hkv, d), dt, std, bwd in whole:
+    whole = [("fp32_L1K_M16_h4_d64_fwd", 0, (1, 1024, 16, 4, 4, 64), torch.float32, 1.0, False, 0),
+             ("bf16_L8K_M32_b2_h16kv8", 1, (2, 8192, 32, 16, 8, 128), torch.bfloat16, 128 ** -0.5, True, 0),
+             ("bf16_L64K_M32_h40kv8", 2, (1, 65536, 32, 40, 8, 128), torch.bfloat16, 1.0, True, 0),
+             # the 64K workload under a 1,024-token clean-key sliding window
+             ("bf16_L64K_M32_h40kv8_window1024", 2, (1, 65536, 32, 40, 8, 128), torch.bfloat16, 1.0, True,
+              1024)]
+    for name, idx, (batch, L, M, hq, hkv, d), dt, std, bwd, window in whole:
         seed = synth.SEED_BASE + idx
         n2 = 2 * L
         q = synth.normal((batch, n2, hq, d), seed, "q", dev, dt, std)
         k = synth.normal((batch, n2, hkv, d), seed, "k", dev, dt, std)
         v = synth.normal((batch, n2, hkv, d), seed, "v", dev, dt, std)
         do = synth.normal((batch, n2, hq, d), seed, "do", dev, torch.bfloat16)
-        wm = WholeMask(batch, L, M, hq, hkv, d, B.BDATTN_F32 if dt == torch.float32 else B.BDATTN_BF16)
+        wm = WholeMask(batch, L, M, hq, hkv, d, B.BDATTN_F32 if dt == torch.float32 else B.BDATTN_BF16,
+                       window=window)
         wf, wb = wm.workspace(False, dev), wm.workspace(True, dev)
         grads = wm.alloc_grads(dev)
         state = {}
@@ -176,7 +196,7 @@ def report_all(reps=3):
                 wm.bwd(q, k, v, state["o"], state["lse"], do, ws=wb, grads=grads)
 
         ms = timed(step)
-        pairs = visible_pairs(L, M) * hq * batch
+        pairs = visible_pairs(L, M, window) * hq * batch
         flops = (14 if bwd else 4) * d * pairs
         rows.append((name, ms, flops, batch * L))
         del q, k, v, do, wm, wf, wb, grads, state
