@@ -150,7 +150,10 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
 
 // Contraction over the step's rows: acc^T[d][key] += T^T[d][row] X[row][key]
 // with T a staged row tile (read across its rows) and X (P or dS) in
-// registers.
+// registers.  The products are compiler builtins (accumulators in VGPRs),
+// so the compiler inserts every wait state around them; a schedule with
+// these products as inline assembly (AGPR accumulators) gave wrong dK once
+// they ran one step behind the exponentials.
 template <int D>
 __device__ __forceinline__ void rows_contract(const _Float16* tile, const LaneOff<D>& o,
                                               const f16x8 (&x)[kRB][kKB][2], f32x16 (&acc)[D / 32][kKB]) {
@@ -168,7 +171,7 @@ __device__ __forceinline__ void rows_contract(const _Float16* tile, const LaneOf
     }
     const int s = f / NDB, db = f % NDB;
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) mfma_f16_agpr(acc[db][kb], fr[f], x[s >> 1][kb][s & 1]);
+    for (int kb = 0; kb < kKB; ++kb) acc[db][kb] = mfma_f16(fr[f], x[s >> 1][kb][s & 1], acc[db][kb]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -324,7 +327,6 @@ __device__ __forceinline__ void dkdv_role(const Plan& P, const DkdvArgs& A, Dkdv
     for (int kb = 0; kb < kKB; ++kb) acc[db][kb] = f32x16{};
   if (total > 0)
     dkdv_walk<D, S_WAVE>(P, A, sm, K, b, g, kvalid, kt1, wave, kw, lane, ql, hh, mysrc, nseg, total, o, kvreg, acc);
-  agpr_settle();
   const float f = S_WAVE ? 1.f : P.scale;
 #pragma unroll
   for (int kb = 0; kb < kKB; ++kb) {
