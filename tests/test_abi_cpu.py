@@ -135,6 +135,10 @@ def test_invalid_arguments_rejected_on_host():
         st = _status(B.bdattn_fwd, p, s, k, None, None, None, None, None, None, None, B.BDATTN_BF16, None, None,
                      0)
         assert st == B.BDATTN_EINVAL, (p.L, p.M, st)
+    # a share with no rows computes nothing and touches nothing: OK before any HIP call
+    empty = B.share([], [])
+    assert _status(B.bdattn_fwd, ok_p, empty, ok_k, None, None, None, None, None, None, None, B.BDATTN_BF16,
+                   None, None, 0) == B.BDATTN_OK
     # unsupported head dim and dtype combinations are reported as such
     p96 = B.problem(1, 1024, 16, 4, 2, 96)
     assert _status(B.bdattn_fwd, p96, ok_s, ok_k, None, None, None, None, None, None, None, 0, None, None, 0) \

@@ -1,0 +1,109 @@
+"""GPU edge cases of the boundary: a call whose key set is empty, a call
+with only the share's own corrupted keys (the local block-diagonal part),
+and a share made of clean query rows only.  Each is checked against the
+oracle on the same rows, or against the documented identity of an empty
+call (O = 0, LSE = -inf, gradient accumulators left untouched)."""
+import numpy as np
+import pytest
+import torch
+
+from tests.common import TOL_GRAD, TOL_LSE, TOL_O, csbp_inputs, doubled_host, max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_lm_bdlm_amd import bdattn
+    bdattn.lib()
+    return torch.device("cuda:0")
+
+
+def _ins(t):
+    return t["q_clean"], t["q_corr"], t["k_clean"], t["v_clean"], t["k_corr"], t["v_corr"]
+
+
+def test_empty_key_set(dev):
+    """No clean range and no local keys: every row gets O = 0 and LSE = -inf,
+    and the backward adds nothing to any accumulator."""
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd.runner import CsbpShare
+    L, M, hq, hkv, d = 256, 16, 4, 2, 128
+    blocks, clean_q = [1, 5, 14], [(32, 96)]
+    t = csbp_inputs(400, L, M, hq, hkv, d, blocks, clean_q, device=dev)
+    full = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, [[(0, L)]])
+    o32, lse_f, _ = full.fwd(*_ins(t))
+    empty = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, [[]])
+    kv = empty.kv_shards[0]
+    ws = empty.workspace(True, dev)
+    o = torch.full((1, empty.R, hq, d), 7.0, dtype=torch.float32, device=dev)
+    lse = torch.full((1, empty.R, hq), 7.0, dtype=torch.float32, device=dev)
+    B.bdattn_fwd(empty.prob, empty.share, kv, *_ins(t), o, B.BDATTN_F32, lse, ws)
+    grads = empty.alloc_grads(dev)
+    for g in grads[:5]:
+        g.fill_(3.0)
+    dq, dkc, dvc, dkx, dvx, delta = grads
+    B.bdattn_bwd(empty.prob, empty.share, kv, *_ins(t), o32, B.BDATTN_F32, lse_f, t["do"], delta, 0,
+                 dq, dkc, dvc, dkx, dvx, ws)
+    torch.cuda.synchronize()
+    assert (o == 0).all() and torch.isneginf(lse).all()
+    for g in grads[:5]:
+        assert (g == 3.0).all()
+    assert torch.isfinite(delta).all()  # D is still computed for later calls
+
+
+@pytest.mark.parametrize("L,M,hq,hkv,d,blocks", [(256, 16, 4, 2, 128, [0, 3, 9, 15]), (384, 32, 2, 1, 64, [2, 11])])
+def test_local_only_call(dev, orc, L, M, hq, hkv, d, blocks):
+    """Only the share's own corrupted keys: the block-diagonal part alone
+    ('CSBP 完全拆解', the local attention that runs before any clean shard)."""
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd.runner import CsbpShare
+    t = csbp_inputs(410 + L, L, M, hq, hkv, d, blocks, [], device=dev)
+    sh = CsbpShare(1, L, M, hq, hkv, d, blocks, [], [])
+    ws = sh.workspace(True, dev)
+    o = torch.empty(1, sh.R, hq, d, dtype=torch.float32, device=dev)
+    lse = torch.empty(1, sh.R, hq, dtype=torch.float32, device=dev)
+    B.bdattn_fwd(sh.prob, sh.share, sh.kv_local, *_ins(t), o, B.BDATTN_F32, lse, ws)
+    grads = sh.alloc_grads(dev)
+    dq, dkc, dvc, dkx, dvx, delta = grads
+    B.bdattn_bwd(sh.prob, sh.share, sh.kv_local, *_ins(t), o, B.BDATTN_F32, lse, t["do"], delta, 0,
+                 dq, dkc, dvc, dkx, dvx, ws)
+    torch.cuda.synchronize()
+    q, k, v, do, pos = doubled_host(L, hq, hkv, d, t, blocks, [], M)
+    p = orc.problem(1, L, M, hq, hkv, d, bf16=True)
+    local = orc.keys([], local=True)
+    o_ref, lse_ref = orc.fwd(p, local, q, k, v)
+    assert max_abs(o.cpu().numpy()[0], o_ref[0, pos]) <= TOL_O
+    assert max_abs(lse.cpu().numpy()[0], lse_ref[0, pos]) <= TOL_LSE
+    sh_o = orc.share(L, M, blocks=blocks)
+    dq_ref, dk_ref, dv_ref = orc.bwd(p, sh_o, local, local, q, k, v, do)
+    assert rel_l2(dq.cpu().numpy()[0], dq_ref[0, pos]) <= TOL_GRAD
+    assert rel_l2(dkx.cpu().numpy()[0], dk_ref[0, pos]) <= TOL_GRAD
+    assert rel_l2(dvx.cpu().numpy()[0], dv_ref[0, pos]) <= TOL_GRAD
+    assert (dkc == 0).all() and (dvc == 0).all()  # no clean key in the call
+
+
+def test_clean_rows_only_share(dev, orc):
+    """A share of clean query rows only (two ranges, no blocks) against two
+    zigzag clean shards merged by LSE."""
+    from block_diffusion_lm_bdlm_amd.runner import CsbpShare
+    L, M, hq, hkv, d = 512, 16, 4, 2, 128
+    clean_q = [(64, 160), (400, 512)]
+    shards = [[(0, 64), (448, 512)], [(64, 448)]]
+    t = csbp_inputs(420, L, M, hq, hkv, d, [], clean_q, device=dev)
+    sh = CsbpShare(1, L, M, hq, hkv, d, [], clean_q, shards)
+    o32, lse, _ = sh.fwd(*_ins(t))
+    dq, dkc, dvc, _, _, _ = sh.bwd(*_ins(t), o32, lse, t["do"])
+    torch.cuda.synchronize()
+    q, k, v, do, pos = doubled_host(L, hq, hkv, d, t, [], clean_q, M)
+    p = orc.problem(1, L, M, hq, hkv, d, bf16=True)
+    o_ref, lse_ref = orc.fwd(p, orc.keys(), q, k, v)
+    assert max_abs(o32.cpu().numpy()[0], o_ref[0, pos]) <= TOL_O
+    assert max_abs(lse.cpu().numpy()[0], lse_ref[0, pos]) <= TOL_LSE
+    sh_o = orc.share(L, M, clean=clean_q)
+    dq_ref, dk_ref, dv_ref = orc.bwd(p, sh_o, orc.keys(), orc.keys(), q, k, v, do)
+    assert rel_l2(dq.cpu().numpy()[0], dq_ref[0, pos]) <= TOL_GRAD
+    assert rel_l2(dkc.cpu().numpy()[0], dk_ref[0, :L]) <= TOL_GRAD
+    assert rel_l2(dvc.cpu().numpy()[0], dv_ref[0, :L]) <= TOL_GRAD
