@@ -124,10 +124,16 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = wave_max32(mx);
-      const float m_new = fmaxf(m_run, mx);
+      // The running max moves only when the tile's max exceeds it by more
+      // than 8 (base 2, after scaling): probabilities then stay <= 2^8, which
+      // fp16 P and the fp32 sums hold as well as values <= 1, and O is
+      // rescaled only on such jumps instead of on every increase.  LSE uses
+      // whichever max was kept, so it is unchanged.
+      const bool grow = mx * c2 > m_run * c2 + 8.f;
+      const float m_new = grow ? mx : m_run;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float mc = m_use * c2;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c2 - mc);
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run * c2 - mc) : 1.f;
       float lsum = 0.f;
       f16x8 pf[2][2];
 #pragma unroll
