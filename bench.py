@@ -155,15 +155,20 @@ def report_all(reps=3):
     dev = torch.device("cuda:0")
 
     def timed(fn):
+        """Average ms per call and each kernel's average ms per call."""
         fn()
         torch.cuda.synchronize()
+        B.bdattn_profile_read()
+        B.bdattn_profile_enable(True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        B.bdattn_profile_enable(False)
+        prof = B.bdattn_profile_read()
+        return e0.elapsed_time(e1) / reps, {n: t / reps for n, (_, t) in prof.items()}
 
     rows = []
     whole = [("fp32_L1K_M16_h4_d64_fwd", 0, (1, 1024, 16, 4, 4, 64), torch.float32, 1.0, False, 0),
@@ -195,10 +200,10 @@ def report_all(reps=3):
                     g_.zero_()
                 wm.bwd(q, k, v, state["o"], state["lse"], do, ws=wb, grads=grads)
 
-        ms = timed(step)
+        ms, kern = timed(step)
         pairs = visible_pairs(L, M, window) * hq * batch
         flops = (14 if bwd else 4) * d * pairs
-        rows.append((name, ms, flops, batch * L))
+        rows.append((name, ms, flops, batch * L, kern))
         del q, k, v, do, wm, wf, wb, grads, state
         torch.cuda.empty_cache()
     shares = [("csbp_L256K_P8_r0_h32kv8", 3, 262144, 32, 32, 8, 8, False, 0.0),
@@ -233,20 +238,23 @@ def report_all(reps=3):
                 g_.zero_()
             sh.bwd(qc, qx, kc, vc, kx, vx, o32, lse, do, ws=wb, grads=grads)
 
-        ms = timed(step)
+        ms, kern = timed(step)
         flops = 14 * d * share_pairs(L, M, blocks, clean_q) * hq
-        rows.append((name, ms, flops, L // P))
+        rows.append((name, ms, flops, L // P, kern))
         del qc, qx, kx, vx, kc, vc, sh, do, wf, wb, grads
         torch.cuda.empty_cache()
     print(f"{'workload':36s} {'ms':>9s} {'useful TF/s':>12s} {'% of 2.5PF':>10s} {'tokens/s':>12s}",
           file=sys.stderr)
-    for name, ms, flops, toks in rows:
+    for name, ms, flops, toks, kern in rows:
         tf = flops / (ms * 1e-3) / 1e12
         print(f"{name:36s} {ms:9.2f} {tf:12.1f} {100 * tf / PEAK_BF16_TFLOPS:10.2f} {toks / (ms * 1e-3):12.0f}",
               file=sys.stderr)
+        print("    kernels (ms per step): " + ", ".join(f"{n} {t:.3f}" for n, t in sorted(kern.items(), key=lambda x: -x[1])),
+              file=sys.stderr)
         print(json.dumps({"workload": name, "ms": round(ms, 3), "useful_tflops": round(tf, 2),
                           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "tokens_per_s": round(toks / (ms * 1e-3), 1)}), flush=True)
+                          "tokens_per_s": round(toks / (ms * 1e-3), 1),
+                          "kernels_ms": {n: round(t, 4) for n, t in kern.items()}}), flush=True)
 
 
 def main():

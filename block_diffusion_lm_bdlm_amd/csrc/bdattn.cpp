@@ -164,9 +164,7 @@ struct FwdWs {
   _Float16* vt;
 };
 struct BwdWs {
-  _Float16* kh;
-  uint16_t* vn;
-  uint16_t *qn, *don;
+  _Float16 *kh, *vh;
   _Float16 *qh, *doh;
   float *lse2, *dc;
   int32_t* vis;
@@ -190,9 +188,7 @@ size_t carve_bwd(const Plan& P, char* base, BwdWs* w) {
   const size_t nr = (size_t)P.batch * P.hq * P.nqc;
   BwdWs t;
   t.kh = cv.take<_Float16>(nk);
-  t.vn = cv.take<uint16_t>(nk);
-  t.qn = cv.take<uint16_t>(nq);
-  t.don = cv.take<uint16_t>(nq);
+  t.vh = cv.take<_Float16>(nk);
   t.qh = cv.take<_Float16>(nq);
   t.doh = cv.take<_Float16>(nq);
   t.lse2 = cv.take<float>(nr);
@@ -214,9 +210,8 @@ bool tensor_ok(const bdattn_tensor& t, int elem_bytes) {
 TensorArg targ(const bdattn_tensor& t) { return TensorArg{t.ptr, t.batch_stride, t.row_stride, t.head_stride}; }
 
 // ------------------------------------------------------------------ profiling
-enum Kind { K_PACK_K, K_PACK_Q, K_FWD, K_FWD_F32, K_DELTA, K_DQ, K_DKDV, K_MERGE, K_COUNT };
-const char* kKindNames[K_COUNT] = {"pack_k", "pack_q", "fwd_bf16", "fwd_f32",
-                                   "delta",  "dq",     "dkdv",     "merge"};
+enum Kind { K_PACK_K, K_PACK_Q, K_FWD, K_FWD_F32, K_DQ, K_DKDV, K_MERGE, K_COUNT };
+const char* kKindNames[K_COUNT] = {"pack_k", "pack_q", "fwd_bf16", "fwd_f32", "dq", "dkdv", "merge"};
 
 struct Prof {
   std::mutex mu;
@@ -433,15 +428,11 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   BwdWs ws;
   carve_bwd(P, static_cast<char*>(workspace), &ws);
-  hipError_t e;
-  if (!delta_ready) {
-    DeltaArgs da{targ(o_final), o_dtype == BDATTN_F32, targ(d_o), delta};
-    e = timed(K_DELTA, s, [&] { return launch_delta(P, da, s); });
-    if (e != hipSuccess) return BDATTN_EHIP;
-  }
-  PackQArgs pq{targ(q_clean), targ(q_corr), targ(d_o), lse_final, delta, ws.qn, ws.don, ws.qh, ws.doh,
+  // pack_q also forms D = rowsum(dO * O) unless the caller gives it
+  PackQArgs pq{targ(q_clean), targ(q_corr), targ(d_o), delta_ready ? TensorArg{} : targ(o_final),
+               o_dtype == BDATTN_F32, delta_ready != 0, lse_final, delta, ws.qh, ws.doh,
                ws.lse2, ws.dc, ws.vis};
-  e = timed(K_PACK_Q, s, [&] { return launch_pack_q(P, pq, s); });
+  hipError_t e = timed(K_PACK_Q, s, [&] { return launch_pack_q(P, pq, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   if (P.nkc == 0) return BDATTN_OK;  // no key in this call: nothing to add
   PackKArgs pk;
@@ -451,14 +442,14 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   pk.k_corr = targ(k_corr);
   pk.v_corr = targ(v_corr);
   pk.kh = ws.kh;
-  pk.vn = ws.vn;
+  pk.vh = ws.vh;
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kh, ws.vn,
+  DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kh, ws.vh,
               dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc};
   e = timed(K_DKDV, s, [&] { return launch_dkdv(P, ka, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DqArgs qa{ws.qh, ws.don, ws.lse2, ws.dc, ws.kh, ws.vn, dq_acc};
+  DqArgs qa{ws.qh, ws.doh, ws.lse2, ws.dc, ws.kh, ws.vh, dq_acc};
   return hip_status(timed(K_DQ, s, [&] { return launch_dq(P, qa, s); }));
 }
 

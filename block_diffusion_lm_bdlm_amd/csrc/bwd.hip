@@ -28,11 +28,11 @@ namespace {
 //   S^T = K Q^T,  P^T = exp(S^T - LSE) (masked),  dP^T = V dO^T,
 //   dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T,
 // reading each K, V and K^T fragment from LDS once for both row blocks.
-// K (fp16 rows) and V (bf16 rows) go from global memory straight into LDS
+// K and V (fp16 rows) go from global memory straight into LDS
 // (global_load_lds), double buffered; K^T fragments are read across the
-// rows of the staged K tile with the transposing LDS read.  S^T and dQ^T
-// run as fp16 products (Q, K converted exactly by the packing), dP^T in
-// bf16.
+// rows of the staged K tile with the transposing LDS read.  Every product
+// runs in fp16 on Q, dO, K and V as converted by the packing (the values of
+// the bf16 inputs).
 constexpr int kDqWaves = 2;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRows = kBQ / kDqWaves;  // query rows per wave
@@ -43,7 +43,7 @@ template <int D>
 struct __attribute__((aligned(16))) DqSmem {
   static constexpr int TILE = kBK * D;  // elements per staged tile
   _Float16 k[2][TILE];                  // fp16 [key][d]
-  uint16_t v[2][TILE];                  // bf16 [key][d]
+  _Float16 v[2][TILE];
 };
 
 template <int D>
@@ -64,7 +64,7 @@ __device__ __forceinline__ void dq_stage_kv(const DqArgs& A, const Plan& P, int 
     const int blk = (wave + kDqWaves * j) * 512;
     const int64_t e = base + (int64_t)j * kDqWaves * 512;
     copy16(A.kh + e, o.dn[j & 1], &sm.k[B][blk]);
-    copy16(A.vn + e, o.dn[j & 1], &sm.v[B][blk]);
+    copy16(A.vh + e, o.dn[j & 1], &sm.v[B][blk]);
   }
 }
 
@@ -141,7 +141,7 @@ __device__ __forceinline__ void dq_ds_piece(int q, int kb, int ss, const f32x16 
 template <int D>
 __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t c, const DqRows& rw, float c2,
                                         int ql, int hh, const f16x8 (&qreg)[2][D / 16],
-                                        const bf16x8 (&doreg)[2][D / 16], const LaneOff<D>& o,
+                                        const f16x8 (&doreg)[2][D / 16], const LaneOff<D>& o,
                                         f32x16 (&dqacc)[2][D / 32]) {
   constexpr int NF = 2 * (D / 16);  // K or V fragments (ks, kb)
   // S^T
@@ -164,25 +164,25 @@ __device__ __forceinline__ void dq_step(DqSmem<D>& sm, int B, bool full, int32_t
   f32x16 pc[2][2];
   {
     constexpr int PE = 64 / NF;  // probabilities per fragment
-    const uint16_t* tb = sm.v[B] + ql * D;
-    bf16x8 fr[NF];
+    const _Float16* tb = sm.v[B] + ql * D;
+    f16x8 fr[NF];
 #pragma unroll
-    for (int f = 0; f < kAhead; ++f) fr[f] = ld16<bf16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
+    for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if (f + kAhead < NF) {
         const int h = f + kAhead;
-        fr[h] = ld16<bf16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
+        fr[h] = ld16<f16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
       }
       const int kb = f & 1, ks = f >> 1;
       // each product is followed by half of this fragment's probabilities
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         if (ks == 0)
-          pc[rb][kb] = mfma_bf16_bagpr0(fr[f], doreg[rb][ks]);
+          pc[rb][kb] = mfma_f16_bagpr0(fr[f], doreg[rb][ks]);
         else
-          mfma_bf16_bagpr(pc[rb][kb], fr[f], doreg[rb][ks]);
+          mfma_f16_bagpr(pc[rb][kb], fr[f], doreg[rb][ks]);
 #pragma unroll
         for (int e = rb * (PE / 2); e < (rb + 1) * (PE / 2); ++e) {
           const int x = f * PE + e, prb = x >> 5, pkb = (x >> 4) & 1, i = x & 15;
@@ -238,7 +238,7 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
 
   // Q and dO of this lane's two rows (B operands, kept in AGPRs)
   f16x8 qreg[2][D / 16];
-  bf16x8 doreg[2][D / 16];
+  f16x8 doreg[2][D / 16];
   DqRows rw;
   RowBounds rbd[2];
 #pragma unroll
@@ -248,7 +248,7 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       qreg[rb][ks] = ld16<f16x8>(A.qh + cr * D + ks * 16 + hh * 8);
-      doreg[rb][ks] = ld16<bf16x8>(A.don + cr * D + ks * 16 + hh * 8);
+      doreg[rb][ks] = ld16<f16x8>(A.doh + cr * D + ks * 16 + hh * 8);
       keep_in_agpr(qreg[rb][ks]);
       keep_in_agpr(doreg[rb][ks]);
     }

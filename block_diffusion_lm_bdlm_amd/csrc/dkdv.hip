@@ -26,8 +26,8 @@
 // XOR-swizzled by row.  S and dP read the tiles along their rows; the
 // contractions over rows (dV, dK) read the same tiles across their rows
 // with the transposing LDS read, so each operand is staged once.  All
-// products run in fp16 (V is converted once on load; Q, dO and K come
-// converted): the values are those of the bf16 inputs.
+// products run in fp16 (Q, dO, K and V come converted by the packing): the
+// values are those of the bf16 inputs.
 // The walk runs back to front by position (all heads of the group at each
 // position): the last rows are seen by every key tile, so the workgroups
 // resident on one XCD stay on the same rows and share them through L2.
@@ -317,7 +317,7 @@ __device__ __forceinline__ void dkdv_role(const Plan& P, const DkdvArgs& A, Dkdv
         if constexpr (S_WAVE)
           kvreg[kb][ks] = ld16<f16x8>(A.kh + e);
         else
-          kvreg[kb][ks] = bf16x8_to_f16x8(ld16<u32x4>(A.vn + e));
+          kvreg[kb][ks] = ld16<f16x8>(A.vh + e);
       }
   }
   f32x16 acc[D / 32][kKB];  // dV^T (S-wave) or dK^T (P-wave)

@@ -16,13 +16,14 @@ struct TensorArg {
 // ---------------------------------------------------------------- packing
 // Compact key space: the call's key segments back to back, each starting at
 // a multiple of kAlign, zero padded.  Natural layouts are [batch][hkv][nkc][d]
-// (bf16, or fp16 for kh); transposed ones fp16 [batch][hkv][nkc/64][d][64]
-// (tiles of 64 rows, each contiguous) with perm16 groups.
+// (bf16 for kn, fp16 for kh and vh); transposed ones fp16
+// [batch][hkv][nkc/64][d][64] (tiles of 64 rows, each contiguous) with
+// perm16 groups.
 struct PackKArgs {
   TensorArg k_clean, v_clean, k_corr, v_corr;  // bf16
   uint16_t* kn;   // natural K (nullable)
-  uint16_t* vn;   // natural V (nullable)
   _Float16* kh;   // natural K in fp16 (nullable)
+  _Float16* vh;   // natural V in fp16 (nullable)
   _Float16* vt;   // transposed V (nullable)
 };
 
@@ -30,11 +31,12 @@ struct PackKArgs {
 // at rows [tile0 * kBQ, (tile0 + ntiles) * kBQ), zero padded.
 struct PackQArgs {
   TensorArg q_clean, q_corr, d_o;  // bf16
+  TensorArg o;                     // final O (read when !delta_ready)
+  int32_t o_f32;                   // O is fp32 (else bf16)
+  int32_t delta_ready;             // delta given; else D = dO . O is computed and stored
   const float* lse;    // [batch][R][hq]
-  const float* delta;  // [batch][R][hq]
-  uint16_t* qn;        // [batch][hq][nqc][d] bf16
-  uint16_t* don;
-  _Float16* qh;        // [batch][hq][nqc][d] fp16: the same values in half precision
+  float* delta;        // [batch][R][hq]
+  _Float16* qh;        // [batch][hq][nqc][d] fp16: the bf16 values in half precision
   _Float16* doh;
   float* lse2;         // [batch][hq][nqc] log2-scaled LSE; +inf on padding rows
   float* dc;           // [batch][hq][nqc] delta; 0 on padding rows
@@ -59,20 +61,13 @@ struct FwdF32Args {
   float* lse;
 };
 
-struct DeltaArgs {
-  TensorArg o;  // bf16 or fp32 (o_f32)
-  int32_t o_f32;
-  TensorArg d_o;  // bf16
-  float* delta;   // [batch][R][hq]
-};
-
 struct DqArgs {
-  const _Float16* qh;  // compact query side (Q fp16, dO bf16)
-  const uint16_t* don;
+  const _Float16* qh;  // compact query side, fp16 natural
+  const _Float16* doh;
   const float* lse2;
   const float* dc;
-  const _Float16* kh;  // compact key side (K fp16, V bf16)
-  const uint16_t* vn;
+  const _Float16* kh;  // compact key side, fp16 natural
+  const _Float16* vh;
   float* dq;  // [batch][R][hq][d], +=
 };
 
@@ -83,7 +78,7 @@ struct DkdvArgs {
   const float* dc;
   const int32_t* vis;
   const _Float16* kh;
-  const uint16_t* vn;
+  const _Float16* vh;
   float* dk_clean;  // [batch][L][hkv][d], +=
   float* dv_clean;
   float* dk_corr;   // [batch][n_corr_rows][hkv][d], +=
@@ -104,7 +99,6 @@ hipError_t launch_pack_k(const Plan& P, const PackKArgs& a, hipStream_t s);
 hipError_t launch_pack_q(const Plan& P, const PackQArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const Plan& P, const FwdF32Args& a, hipStream_t s);
-hipError_t launch_delta(const Plan& P, const DeltaArgs& a, hipStream_t s);
 hipError_t launch_dq(const Plan& P, const DqArgs& a, hipStream_t s);
 hipError_t launch_dkdv(const Plan& P, const DkdvArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);

@@ -2,16 +2,18 @@
 //
 //  pack_k: gathers the call's key rows (clean token ranges, then the share's
 //          packed corrupted rows) into one compact, zero-padded key space;
-//          writes the layouts its consumer asks for: natural bf16 K/V,
-//          natural fp16 K, transposed fp16 V^T.  The transposed copy is tiled: each tile of 64 rows is one contiguous [d][64] block
+//          writes the layouts its consumer asks for: natural bf16 K,
+//          natural fp16 K and V, transposed fp16 V^T.  The transposed copy is tiled: each tile of 64 rows is one contiguous [d][64] block
 //          (so a consumer's tile is a single 16 KB read), and every aligned
 //          group of 16 rows is in perm16 order, the order in which an MFMA C
 //          tile delivers its rows as a B operand.
-//  pack_q: the same for the share's query side of the backward (Q, dO,
-//          natural bf16 and natural fp16), plus log2-scaled LSE and delta
-//          per row and each row's visible key interval per key kind.
-//  delta:  D_i = sum_t dO_i[t] O_i[t], the softmax backward's row term.
-// All three are bandwidth-bound copies; none changes a value except the
+//  pack_q: the same for the share's query side of the backward (Q and dO,
+//          natural fp16), plus log2-scaled LSE and D per row and each
+//          row's visible key interval per key kind.  Unless the caller
+//          gives D, it is formed here from the dO row being packed and the
+//          final O: D_i = sum_t dO_i[t] O_i[t], the softmax backward's row
+//          term, and stored for later calls.
+// Both are bandwidth-bound copies; neither changes a value except the
 // bf16 -> fp16 conversions (exact for values in the half range and above
 // its subnormals).
 #include "device.h"
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
     }
     const int64_t nat = ((int64_t)(b * P.hkv + g) * P.nkc + cc) * D + dc;
     if (A.kn) *reinterpret_cast<u32x4*>(A.kn + nat) = kv;
-    if (A.vn) *reinterpret_cast<u32x4*>(A.vn + nat) = vv;
     if (A.kh) *reinterpret_cast<f16x8*>(A.kh + nat) = bf16x8_to_f16x8(kv);
+    if (A.vh) *reinterpret_cast<f16x8*>(A.vh + nat) = bf16x8_to_f16x8(vv);
     *reinterpret_cast<u32x4*>(&sm.b[r][dc]) = vv;
   }
   if (A.vt) {
@@ -86,6 +88,9 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
 
 template <int D>
 __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQArgs A) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row: consecutive lanes of one wave
+  static_assert(kPT * CPR % 256 == 0 && 64 % CPR == 0, "every lane runs every chunk loop; rows within a wave");
+  __shared__ float dsum[kPT];
   const int tid = threadIdx.x;
   const int32_t c = blockIdx.x * kPT;  // compact query row
   const int h = blockIdx.y, b = blockIdx.z;
@@ -98,18 +103,42 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
     const int r = ch / (D / 8), dc = (ch % (D / 8)) * 8;
     const int32_t rr = rbase + r;
     u32x4 qv = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
+    float dd = 0.f;  // this chunk's part of D
     if (rr < S.nrows) {
       qv = ldg16(static_cast<const uint16_t*>(QT.p) + b * QT.bs + (int64_t)(S.src0 + rr) * QT.rs +
                  (int64_t)h * QT.hs + dc);
       dv = ldg16(static_cast<const uint16_t*>(A.d_o.p) + b * A.d_o.bs + (int64_t)(S.row0 + rr) * A.d_o.rs +
                  (int64_t)h * A.d_o.hs + dc);
+      if (!A.delta_ready) {
+        const int64_t oo = b * A.o.bs + (int64_t)(S.row0 + rr) * A.o.rs + (int64_t)h * A.o.hs + dc;
+        float ov[8];
+        if (A.o_f32) {
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(A.o.p) + oo);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(A.o.p) + oo + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ov[e] = a0[e];
+            ov[e + 4] = a1[e];
+          }
+        } else {
+          const u32x4 ob = ldg16(static_cast<const uint16_t*>(A.o.p) + oo);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ov[e] = bf16_to_f32((uint16_t)(ob[e >> 1] >> (16 * (e & 1))));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dd = fmaf(bf16_to_f32((uint16_t)(dv[e >> 1] >> (16 * (e & 1)))), ov[e], dd);
+      }
+    }
+    if (!A.delta_ready) {  // sum over the row's CPR lanes
+#pragma unroll
+      for (int m = CPR / 2; m >= 1; m >>= 1) dd += __shfl_xor(dd, m, CPR);
+      if (dc == 0) dsum[r] = dd;
     }
     const int64_t nat = (hb * P.nqc + c + r) * D + dc;
-    *reinterpret_cast<u32x4*>(A.qn + nat) = qv;
-    *reinterpret_cast<u32x4*>(A.don + nat) = dv;
     *reinterpret_cast<f16x8*>(A.qh + nat) = bf16x8_to_f16x8(qv);
     *reinterpret_cast<f16x8*>(A.doh + nat) = bf16x8_to_f16x8(dv);
   }
+  __syncthreads();  // dsum
   if (tid < kPT) {
     const int32_t rr = rbase + tid;
     float l2 = INFINITY, dd = 0.f;
@@ -119,7 +148,12 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
       // a row that sees no key (LSE = -inf) has O = 0 and no gradient: +inf
       // makes every recomputed probability exp2(s - inf) vanish.
       l2 = lse == -INFINITY ? INFINITY : lse * 1.4426950408889634f;
-      dd = A.delta[idx];
+      if (A.delta_ready) {
+        dd = A.delta[idx];
+      } else {
+        dd = dsum[tid];
+        A.delta[idx] = dd;
+      }
     }
     A.lse2[hb * P.nqc + c + tid] = l2;
     A.dc[hb * P.nqc + c + tid] = dd;
@@ -138,34 +172,6 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
       for (int k = 0; k < 4; ++k) A.vis[(int64_t)k * P.nqc + c + tid] = v[k];
     }
   }
-}
-
-// D_i = dO_i . O_i: 16 lanes per (batch, row, head), 8 elements per lane.
-__global__ __launch_bounds__(256) void delta_kernel(const Plan P, const DeltaArgs A, int64_t nrows) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int sub = threadIdx.x & 15;
-  const int64_t r = gid >> 4;
-  float acc = 0.f;
-  const int per = P.d / 16;
-  if (r < nrows) {
-    const int h = (int)(r % P.hq);
-    const int64_t rest = r / P.hq;
-    const int64_t row = rest % P.R, b = rest / P.R;
-    const uint16_t* dop = static_cast<const uint16_t*>(A.d_o.p) + b * A.d_o.bs + row * A.d_o.rs +
-                          (int64_t)h * A.d_o.hs + sub * per;
-    if (A.o_f32) {
-      const float* op = static_cast<const float*>(A.o.p) + b * A.o.bs + row * A.o.rs + (int64_t)h * A.o.hs +
-                        sub * per;
-      for (int t = 0; t < per; ++t) acc = fmaf(bf16_to_f32(dop[t]), op[t], acc);
-    } else {
-      const uint16_t* op = static_cast<const uint16_t*>(A.o.p) + b * A.o.bs + row * A.o.rs +
-                           (int64_t)h * A.o.hs + sub * per;
-      for (int t = 0; t < per; ++t) acc = fmaf(bf16_to_f32(dop[t]), bf16_to_f32(op[t]), acc);
-    }
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (r < nrows && sub == 0) A.delta[r] = acc;
 }
 
 }  // namespace
@@ -187,14 +193,6 @@ hipError_t launch_pack_q(const Plan& P, const PackQArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(pack_q_kernel<128>, grid, dim3(256), 0, s, P, a);
   else
     hipLaunchKernelGGL(pack_q_kernel<64>, grid, dim3(256), 0, s, P, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_delta(const Plan& P, const DeltaArgs& a, hipStream_t s) {
-  const int64_t nrows = (int64_t)P.batch * P.R * P.hq;
-  if (nrows == 0) return hipSuccess;
-  const int64_t blocks = (nrows * 16 + 255) / 256;
-  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P, a, nrows);
   return hipGetLastError();
 }
 

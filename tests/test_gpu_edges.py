@@ -1,8 +1,9 @@
 """GPU edge cases of the boundary: a call whose key set is empty, a call
 with only the share's own corrupted keys (the local block-diagonal part),
-and a share made of clean query rows only.  Each is checked against the
-oracle on the same rows, or against the documented identity of an empty
-call (O = 0, LSE = -inf, gradient accumulators left untouched)."""
+a share made of clean query rows only, and the row term D that the
+backward forms.  Each is checked against the oracle on the same rows, a
+float64 row sum, or the documented identity of an empty call (O = 0,
+LSE = -inf, gradient accumulators left untouched)."""
 import numpy as np
 import pytest
 import torch
@@ -107,3 +108,38 @@ def test_clean_rows_only_share(dev, orc):
     assert rel_l2(dq.cpu().numpy()[0], dq_ref[0, pos]) <= TOL_GRAD
     assert rel_l2(dkc.cpu().numpy()[0], dk_ref[0, :L]) <= TOL_GRAD
     assert rel_l2(dvc.cpu().numpy()[0], dv_ref[0, :L]) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("d,o_f32", [(128, False), (128, True), (64, False)])
+def test_delta_rowsum(dev, d, o_f32):
+    """D = rowsum(dO * O), formed while the backward packs dO ("CSBP 完全拆解",
+    the softmax row term of the chain rule), equals the float64 row sum of
+    the same bf16 dO and O values; a later call with delta_ready reads it
+    back and gives the same gradients bit for bit."""
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd.runner import WholeMask
+    from tests.common import doubled_inputs
+    batch, L, M, hq, hkv = 2, 200, 8, 4, 2
+    q, k, v, do = doubled_inputs(41, batch, L, hq, hkv, d, device=dev)
+    wm = WholeMask(batch, L, M, hq, hkv, d)
+    o, lse = wm.fwd(q, k, v, o_dtype=torch.float32 if o_f32 else torch.bfloat16)
+    grads = wm.alloc_grads(dev)
+    ws = wm.workspace(True, dev)
+    ins = (q[:, :L], q[:, L:], k[:, :L], v[:, :L], k[:, L:], v[:, L:])
+    dq, dkc, dvc, dkx, dvx, delta = grads
+    B.bdattn_bwd(wm.prob, wm.share, wm.kv, *ins, o, B.BDATTN_F32 if o_f32 else B.BDATTN_BF16, lse, do, delta, 0,
+                 dq, dkc, dvc, dkx, dvx, ws)
+    torch.cuda.synchronize()
+    want = (do.double() * o.double()).sum(-1)
+    got = delta.double()
+    assert torch.allclose(got, want, rtol=1e-5, atol=1e-5 * float(want.abs().max()))
+    # the same call with delta given: identical gradients
+    first = [g.clone() for g in grads[:5]]
+    for g in grads[:5]:
+        g.zero_()
+    o_bad = torch.full_like(o, float("nan"))  # not read when delta is given
+    B.bdattn_bwd(wm.prob, wm.share, wm.kv, *ins, o_bad, B.BDATTN_F32 if o_f32 else B.BDATTN_BF16, lse, do, delta,
+                 1, dq, dkc, dvc, dkx, dvx, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(first, grads[:5]):
+        assert torch.equal(a, b)
