@@ -369,7 +369,11 @@ def main():
                    "hkv": hkv, "d": d, "clean_mask": "block-causal", "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(batch * L / (ms * 1e-3), 1),
+        "positions_per_s": round(batch * n2 / (ms * 1e-3), 1),
         "useful_tflop_per_step": round(useful / 1e12, 3),
+        # the stricter count: 12*d per pair (forward 4d, backward 8d without
+        # the recomputed Q K^T)
+        "useful_tflops_12d": round(12.0 / 14.0 * tflops, 2),
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
