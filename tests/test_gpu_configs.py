@@ -9,6 +9,7 @@ compute one at a time, and on identities that hold at any size.
     8 zigzag clean shards of 32768 tokens merged by LSE.
  5. CSBP share, L=524288, M=16, P=16, rank 0 (2048 blocks + its 32768-token
     clean shard of query rows), 32/4 heads, 1% of rows x8 (outlier logits).
+ 3w. workload 3 under a 1,024-token clean-key sliding window.
 
 Sampled checks: O and LSE of random query rows; dQ of random query rows;
 dK/dV of corrupted keys anywhere and of clean keys in the last blocks (few
@@ -57,17 +58,18 @@ def _identities(dq, dk, dv, q, k, v, do, G, hkv):
         assert abs(a - b) <= 1e-2 * scale, (g, a, b, scale)
 
 
-def _whole(dev, orc, batch, L, M, hq, hkv, d, std, seed, n_rows=96):
+def _whole(dev, orc, batch, L, M, hq, hkv, d, std, seed, n_rows=96, window=0):
+    from block_diffusion_lm_bdlm_amd import bdattn as B
     from block_diffusion_lm_bdlm_amd.runner import WholeMask
-    print(f"\n[config] whole mask batch={batch} L={L} M={M} hq={hq} hkv={hkv} d={d}", flush=True)
+    print(f"\n[config] whole mask batch={batch} L={L} M={M} hq={hq} hkv={hkv} d={d} window={window}", flush=True)
     q, k, v, do = doubled_inputs(seed, batch, L, hq, hkv, d, std=std, device=dev)
-    wm = WholeMask(batch, L, M, hq, hkv, d)
+    wm = WholeMask(batch, L, M, hq, hkv, d, B.BDATTN_BF16, window=window)
     o, lse = wm.fwd(q, k, v, o_dtype=torch.bfloat16)
     dq, dk, dv = wm.bwd(q, k, v, o, lse, do)
     torch.cuda.synchronize()
     G = hq // hkv
     hq_, hk_, hv_, hdo = (host_bits(x) for x in (q, k, v, do))
-    p = orc.problem(batch, L, M, hq, hkv, d, bf16=True)
+    p = orc.problem(batch, L, M, hq, hkv, d, bf16=True, window=window)
     rng = np.random.default_rng(seed)
     b = rng.integers(0, batch, n_rows)
     h = rng.integers(0, hq, n_rows)
@@ -76,11 +78,13 @@ def _whole(dev, orc, batch, L, M, hq, hkv, d, std, seed, n_rows=96):
     assert max_abs(o[b, i, h].float().cpu().numpy(), ro) <= TOL_O
     assert max_abs(lse[b, i, h].cpu().numpy(), rl) <= TOL_LSE
     assert rel_l2(dq[b, i, h].cpu().numpy(), rdq) <= TOL_GRAD
-    # keys: corrupted anywhere, clean in the last three blocks
+    # keys: corrupted anywhere; clean in the last three blocks (few rows see
+    # them), or anywhere when a window bounds the rows that see each key
     nk = 24
     kb = rng.integers(0, batch, nk)
     kg = rng.integers(0, hkv, nk)
-    kj = np.concatenate([L + rng.integers(0, L, nk // 2), rng.integers(L - 3 * M, L, nk - nk // 2)])
+    lo = 0 if window > 0 else L - 3 * M
+    kj = np.concatenate([L + rng.integers(0, L, nk // 2), rng.integers(lo, L, nk - nk // 2)])
     rdk, rdv = orc.dkdv_rows(p, orc.share(), orc.keys(), orc.keys(), hq_, hk_, hv_, hdo, kb, kg, kj)
     assert rel_l2(dk[kb, kj, kg].cpu().numpy(), rdk) <= TOL_GRAD
     assert rel_l2(dv[kb, kj, kg].cpu().numpy(), rdv) <= TOL_GRAD
@@ -110,6 +114,12 @@ def test_config2_bf16_L8K(dev, orc):
 
 def test_config3_bf16_L64K(dev, orc):
     _whole(dev, orc, 1, 65536, 32, 40, 8, 128, std=1.0, seed=SEED0 + 2, n_rows=64)
+
+
+def test_config3_window1024(dev, orc):
+    """The headline workload under a 1,024-token clean-key sliding window
+    (the pages' hybrid models attend through such a window in most layers)."""
+    _whole(dev, orc, 1, 65536, 32, 40, 8, 128, std=1.0, seed=SEED0 + 12, n_rows=64, window=1024)
 
 
 def _csbp(dev, orc, L, M, hq, hkv, d, P, r, clean_queries, seed, outlier_frac=0.0, n_rows=64):
