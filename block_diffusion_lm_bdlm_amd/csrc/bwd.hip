@@ -126,7 +126,6 @@ __device__ __forceinline__ void dq_ds_piece(int q, int kb, int ss, const f32x16 
   const int rb = q / H, e0 = (q % H) * W;
 #pragma unroll
   for (int e = e0; e < e0 + W; e += 2) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 t = {(_Float16)(pc[rb][kb][ss * 8 + e] - dval[rb]), (_Float16)(pc[rb][kb][ss * 8 + e + 1] - dval[rb])};
     f16x2 p = {pf[rb][kb][ss][e], pf[rb][kb][ss][e + 1]};
     const f16x2 r = p * t;

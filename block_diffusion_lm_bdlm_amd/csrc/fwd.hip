@@ -12,6 +12,8 @@
 // V^T tiles (fp16) go from global memory straight into LDS
 // (global_load_lds), double buffered, as swizzled tiles.  A key tile that
 // no row sees is never visited; a tile every row sees fully skips the mask.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "stage.h"
@@ -87,8 +89,10 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
     }
     wait_copies();
     __syncthreads();
-    for (int32_t t = 0; t < w.total; ++t) {
-      const int buf = t & 1;
+    // one tile of the walk; the buffer index is a constant in each of the
+    // two unrolled copies, so it folds into the LDS instructions' offsets
+    auto tile_step = [&](int32_t t, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
       int32_t c, ri;
       bool full;
       keywalk_at(w, t, &c, &ri, &full);
@@ -134,16 +138,23 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float mc = m_use * c2;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run * c2 - mc) : 1.f;
-      float lsum = 0.f;
       f16x8 pf[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -mc));
-          lsum += p;
-          pf[kb][i >> 3][i & 7] = (_Float16)p;
-        }
+        for (int i = 0; i < 16; ++i) pf[kb][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -mc));
+      // the normaliser sums the fp16 probabilities the O product uses, two
+      // per instruction (fp32 accumulation)
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const f16x2 pp = {pf[kb][hf][e], pf[kb][hf][e + 1]};
+            lsum = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+          }
       l_run = l_run * alpha + lsum;
       if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -173,7 +184,13 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       __builtin_amdgcn_s_setprio(0);
       wait_copies();
       __syncthreads();  // the next tile's copies have landed; this tile's reads are done
+    };
+    int32_t t = 0;
+    for (; t + 1 < w.total; t += 2) {
+      tile_step(t, std::integral_constant<int, 0>{});
+      tile_step(t + 1, std::integral_constant<int, 1>{});
     }
+    if (t < w.total) tile_step(t, std::integral_constant<int, 0>{});
   }
 
   // epilogue: O = acc / l, LSE = (m * c2 + log2 l) * ln 2
