@@ -32,6 +32,7 @@
 // position): the last rows are seen by every key tile, so the workgroups
 // resident on one XCD stay on the same rows and share them through L2.
 #include <climits>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -261,8 +262,10 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
   stage<D>(A, P, K.kind, hb_of(cur), cq_of(cur), wave, lane, o, sm, 0);
   wait_copies();
   __syncthreads();
-  for (int32_t t = 0; t < total; ++t) {
-    const int B = t & 1;
+  // one step of the walk; the buffer index is a constant in each of the two
+  // unrolled copies, so it folds into the LDS instructions' offsets
+  auto step = [&](int32_t t, auto b_c) {
+    constexpr int B = decltype(b_c)::value;
     const bool more = t + 1 < total;
     StepPos nxt = cur;
     if (more) {
@@ -294,7 +297,13 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
     wait_copies();
     __syncthreads();  // the next step's copies have landed; this step's reads are done
     cur = nxt;
+  };
+  int32_t t = 0;
+  for (; t + 1 < total; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < total) step(t, std::integral_constant<int, 0>{});
 }
 
 // One role of the workgroup on its key tile: this wave's 64 keys in
