@@ -75,6 +75,7 @@ Plan make_plan(const bdattn_problem* p, const bdattn_share* s, const bdattn_kv* 
   P.batch = p->batch;
   P.L = p->L;
   P.M = p->M;
+  P.M_log2 = (P.M & (P.M - 1)) == 0 ? __builtin_ctz((unsigned)P.M) : -1;
   P.hq = p->hq;
   P.hkv = p->hkv;
   P.d = p->d;

@@ -56,6 +56,7 @@ struct KSeg {
 
 struct Plan {
   int32_t batch, L, M, hq, hkv, d, G, token_causal;
+  int32_t M_log2;         // log2(M) when M is a power of two, else -1
   int32_t window;         // clean-key sliding window in tokens (0 = none)
   float scale, scale_log2;
   int32_t R;              // share rows
@@ -134,6 +135,13 @@ struct RowBounds {
 
 // Token position of row 0 of segment s (rows of a segment are consecutive
 // tokens: clean tokens, or the tokens of consecutive blocks).
+// n / M and n % M for n >= 0: a shift and a mask when M is a power of two
+// (every block size the pages use), a division otherwise.
+__host__ __device__ inline int32_t div_M(const Plan& P, int32_t n) { return P.M_log2 >= 0 ? n >> P.M_log2 : n / P.M; }
+__host__ __device__ inline int32_t mod_M(const Plan& P, int32_t n) {
+  return P.M_log2 >= 0 ? n & (P.M - 1) : n % P.M;
+}
+
 __host__ __device__ inline int64_t seg_token0(const Plan& P, const QSeg& s) {
   return s.kind == KIND_CLEAN ? (int64_t)s.first : (int64_t)s.first * P.M;
 }
@@ -142,12 +150,12 @@ __host__ __device__ inline RowBounds row_bounds(const Plan& P, const QSeg& s, in
   RowBounds rb;
   if (s.kind == KIND_CLEAN) {
     const int32_t t = s.first + r;
-    rb.hi_clean = P.token_causal ? t + 1 : (t / P.M + 1) * P.M;
+    rb.hi_clean = P.token_causal ? t + 1 : (div_M(P, t) + 1) * P.M;
     rb.lo_loc = rb.hi_loc = 0;
   } else {
-    const int32_t blk = s.first + r / P.M;
+    const int32_t blk = s.first + div_M(P, r);
     rb.hi_clean = blk * P.M;
-    rb.lo_loc = s.src0 + r - r % P.M;
+    rb.lo_loc = s.src0 + r - mod_M(P, r);
     rb.hi_loc = rb.lo_loc + P.M;
   }
   const int64_t lo = P.window > 0 ? seg_token0(P, s) + r - P.window + 1 : 0;
@@ -229,16 +237,16 @@ __host__ __device__ inline int32_t first_seeing_row(const Plan& P, const QSeg& s
                                                     int32_t k0) {
   if (kkind == KIND_CLEAN) {
     if (s.kind == KIND_CLEAN) {
-      const int32_t tmin = P.token_causal ? k0 : (k0 / P.M) * P.M;
+      const int32_t tmin = P.token_causal ? k0 : div_M(P, k0) * P.M;
       return clampi(tmin - s.first, 0, s.nrows);
     }
-    const int32_t bmin = k0 / P.M + 1;
+    const int32_t bmin = div_M(P, k0) + 1;
     const int64_t r = (int64_t)(bmin - s.first) * P.M;
     return (int32_t)(r < 0 ? 0 : (r > s.nrows ? s.nrows : r));
   }
   if (s.kind == KIND_CLEAN) return s.nrows;
   // packed corrupted key rows: the rows of the same packed block
-  const int32_t pmin = (k0 / P.M) * P.M;
+  const int32_t pmin = div_M(P, k0) * P.M;
   return clampi(pmin - s.src0, 0, s.nrows);
 }
 
@@ -253,7 +261,7 @@ __host__ __device__ inline int32_t end_seeing_row(const Plan& P, const QSeg& s, 
     return (int32_t)(r < 0 ? 0 : (r > s.nrows ? s.nrows : r));
   }
   if (s.kind == KIND_CLEAN) return 0;
-  const int32_t pmax = ((k1 + P.M - 1) / P.M) * P.M;
+  const int32_t pmax = div_M(P, k1 + P.M - 1) * P.M;
   return clampi(pmax - s.src0, 0, s.nrows);
 }
 
