@@ -44,10 +44,18 @@ __device__ __forceinline__ T ld16(const void* p) {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-__device__ __forceinline__ float wave_max32(float x) {  // max with lane ^ 32
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+// Reductions over lanes l and l ^ 32.  v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second; given
+// x twice, every lane receives x of both lanes of its pair (in some order),
+// with no LDS round trip.
+__device__ __forceinline__ float wave_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum32(float x) { return x + __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float wave_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // MFMA C-tile row index of register i for lane half hh.
 __device__ __forceinline__ int crow(int i, int hh) { return (i >> 2) * 8 + hh * 4 + (i & 3); }
