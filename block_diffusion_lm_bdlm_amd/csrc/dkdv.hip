@@ -105,6 +105,7 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
   // fragment f = (rb, ks); kAhead reads stay in flight ahead of the products
   constexpr int NF = kRB * NKS;
   f16x8 fr[NF];
+  f32x4 l4s[kRB][4];  // log2 LSE of this lane's rows, read while the last products run
 #pragma unroll
   for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(qb + (f / NKS) * 32 * D + o.nat[f % NKS]);
   __builtin_amdgcn_sched_barrier(0);
@@ -113,6 +114,12 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
     if (f + kAhead < NF) {
       const int g = f + kAhead;
       fr[g] = ld16<f16x8>(qb + (g / NKS) * 32 * D + o.nat[g % NKS]);
+    }
+    if (f == NF - kAhead) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) l4s[rb][i4] = *reinterpret_cast<const f32x4*>(&sm.lse2[B][rb * 32 + i4 * 8 + hh * 4]);
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -124,7 +131,7 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int r = rb * 32 + i4 * 8 + hh * 4;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[B][r]);
+      const f32x4 l4 = l4s[rb][i4];
       int32_t los[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, his[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
       if constexpr (!FULL) {
         const int4 lo4 = *reinterpret_cast<const int4*>(&sm.vlo[B][r]);
@@ -177,10 +184,11 @@ __device__ __forceinline__ void rows_contract(const _Float16* tile, const LaneOf
   }
 }
 
-// P-wave, first half of a step: dP = dO V^T.
+// P-wave, first half of a step: dP = dO V^T; D of this lane's rows is read
+// while the last products run.
 template <int D>
-__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const f16x8 (&vreg)[kKB][D / 16],
-                                          const LaneOff<D>& o, f32x16 (&pacc)[kRB][kKB]) {
+__device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, int hh, const f16x8 (&vreg)[kKB][D / 16],
+                                          const LaneOff<D>& o, f32x16 (&pacc)[kRB][kKB], f32x4 (&dcs)[kRB][4]) {
   const _Float16* ob = &sm.dO[B][ql * D];
   constexpr int NKS = D / 16, NF = kRB * NKS;
   f16x8 fr[NF];
@@ -193,6 +201,12 @@ __device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const 
       const int g = f + kAhead;
       fr[g] = ld16<f16x8>(ob + (g / NKS) * 32 * D + o.nat[g % NKS]);
     }
+    if (f == NF - kAhead) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) dcs[rb][i4] = *reinterpret_cast<const f32x4*>(&sm.dc[B][rb * 32 + i4 * 8 + hh * 4]);
+    }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
       pacc[f / NKS][kb] = mfma_f16(fr[f], vreg[kb][f % NKS], f % NKS ? pacc[f / NKS][kb] : f32x16{});
@@ -203,14 +217,14 @@ __device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, const 
 // P-wave, second half: dS = P (dP - D) with P from its S-wave (dP - D is
 // rounded to fp16 before the product; dS is an fp16 operand either way).
 template <int D>
-__device__ __forceinline__ void p_phase_ds(DkdvSmem<D>& sm, int B, int kw, int lane, int hh,
+__device__ __forceinline__ void p_phase_ds(DkdvSmem<D>& sm, int kw, int lane, const f32x4 (&dcs)[kRB][4],
                                            const f32x16 (&pacc)[kRB][kKB], f16x8 (&dsf)[kRB][kKB][2]) {
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dc[B][rb * 32 + (2 * ss) * 8 + hh * 4]);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dc[B][rb * 32 + (2 * ss + 1) * 8 + hh * 4]);
+      const f32x4 d0 = dcs[rb][2 * ss];
+      const f32x4 d1 = dcs[rb][2 * ss + 1];
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         const f16x8 p = ld16<f16x8>(&sm.xchg[kw][rb][kb][ss][lane][0]);
@@ -288,10 +302,11 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
       rows_contract<D>(sm.dO[B], o, pf, acc);  // dV^T += dO^T P
     } else {
       f32x16 pacc[kRB][kKB];
-      p_phase_a<D>(sm, B, ql, kvreg, o, pacc);
+      f32x4 dcs[kRB][4];
+      p_phase_a<D>(sm, B, ql, hh, kvreg, o, pacc, dcs);
       barrier_lds();  // P from the S-waves
       f16x8 dsf[kRB][kKB][2];
-      p_phase_ds<D>(sm, B, kw, lane, hh, pacc, dsf);
+      p_phase_ds<D>(sm, kw, lane, dcs, pacc, dsf);
       rows_contract<D>(sm.q[B], o, dsf, acc);  // dK^T += Q^T dS
     }
     wait_copies();
