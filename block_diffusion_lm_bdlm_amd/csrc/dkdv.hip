@@ -156,20 +156,32 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
   }
 }
 
-// Contraction over the step's rows: acc^T[d][key] += T^T[d][row] X[row][key]
-// with T a staged row tile (read across its rows) and X (P or dS) in
-// registers.  The products are compiler builtins (accumulators in VGPRs),
-// so the compiler inserts every wait state around them; a schedule with
-// these products as inline assembly (AGPR accumulators) gave wrong dK once
-// they ran one step behind the exponentials.
+// Fragments f = (s, db) of the contraction over rows.  The first kAhead
+// are read by rows_contract_head ahead of the mid-step barrier (the tile is
+// already in LDS), so the barrier's wait covers their latency.
 template <int D>
-__device__ __forceinline__ void rows_contract(const _Float16* tile, const LaneOff<D>& o,
-                                              const f16x8 (&x)[kRB][kKB][2], f32x16 (&acc)[D / 32][kKB]) {
-  // fragment f = (s, db); kAhead reads stay in flight ahead of the products
-  constexpr int NDB = D / 32, NF = (kBQB / 16) * NDB;
-  f16x8 fr[NF];
+constexpr int kRcFrags = (kBQB / 16) * (D / 32);
+template <int D>
+__device__ __forceinline__ void rows_contract_head(const _Float16* tile, const LaneOff<D>& o,
+                                                   f16x8 (&fr)[kRcFrags<D>]) {
+  constexpr int NDB = D / 32;
 #pragma unroll
   for (int f = 0; f < kAhead; ++f) fr[f] = tr_frag<D>(tile + (f / NDB) * 16 * D, o, f % NDB);
+}
+
+// Contraction over the step's rows: acc^T[d][key] += T^T[d][row] X[row][key]
+// with T a staged row tile (read across its rows) and X (P or dS) in
+// registers, continuing from rows_contract_head.  The products are compiler
+// builtins (accumulators in VGPRs), so the compiler inserts every wait state
+// around them; a schedule with these products as inline assembly (AGPR
+// accumulators) gave wrong dK once they ran one step behind the
+// exponentials.
+template <int D>
+__device__ __forceinline__ void rows_contract(const _Float16* tile, const LaneOff<D>& o,
+                                              const f16x8 (&x)[kRB][kKB][2], f32x16 (&acc)[D / 32][kKB],
+                                              f16x8 (&fr)[kRcFrags<D>]) {
+  // kAhead reads stay in flight ahead of the products
+  constexpr int NDB = D / 32, NF = kRcFrags<D>;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
@@ -298,16 +310,20 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
         s_phase_a<D, true>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
       else
         s_phase_a<D, false>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
+      f16x8 fr[kRcFrags<D>];
+      rows_contract_head<D>(sm.dO[B], o, fr);
       barrier_lds();  // P visible to the P-waves
-      rows_contract<D>(sm.dO[B], o, pf, acc);  // dV^T += dO^T P
+      rows_contract<D>(sm.dO[B], o, pf, acc, fr);  // dV^T += dO^T P
     } else {
       f32x16 pacc[kRB][kKB];
       f32x4 dcs[kRB][4];
       p_phase_a<D>(sm, B, ql, hh, kvreg, o, pacc, dcs);
+      f16x8 fr[kRcFrags<D>];
+      rows_contract_head<D>(sm.q[B], o, fr);
       barrier_lds();  // P from the S-waves
       f16x8 dsf[kRB][kKB][2];
       p_phase_ds<D>(sm, kw, lane, dcs, pacc, dsf);
-      rows_contract<D>(sm.q[B], o, dsf, acc);  // dK^T += Q^T dS
+      rows_contract<D>(sm.q[B], o, dsf, acc, fr);  // dK^T += Q^T dS
     }
     wait_copies();
     __syncthreads();  // the next step's copies have landed; this step's reads are done
