@@ -111,6 +111,13 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       __builtin_amdgcn_s_setprio(2);
       scores_2kb<D>(sm.k[buf], ql, qreg, o, sacc);
       __builtin_amdgcn_s_setprio(0);
+      // the first V^T fragments of the O products, read under the softmax;
+      // fragment f = (s, db), s = 16-key step
+      constexpr int NDB = D / 32, NFO = (kBK / 16) * NDB;
+      const _Float16* vtb = sm.vt[buf] + ql * kBK;
+      f16x8 vfr[NFO];
+#pragma unroll
+      for (int f = 0; f < kAhead; ++f) vfr[f] = ld16<f16x8>(vtb + (f % NDB) * 32 * kBK + o.tr[f / NDB]);
       if (!full) {
         int32_t vlo, vhi;
         compact_range(P.k[ri], rb, clean, &vlo, &vhi);
@@ -161,14 +168,12 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       }
       m_run = m_new;
-      // O^T += V^T P^T; fragment f = (s, db), s = 16-key step
+      // O^T += V^T P^T
       __builtin_amdgcn_s_setprio(2);
       {
-        constexpr int NDB = D / 32, NF = (kBK / 16) * NDB;
-        const _Float16* tb = sm.vt[buf] + ql * kBK;
-        f16x8 fr[NF];
-#pragma unroll
-        for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f % NDB) * 32 * kBK + o.tr[f / NDB]);
+        constexpr int NF = NFO;
+        const _Float16* tb = vtb;
+        f16x8 (&fr)[NF] = vfr;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
