@@ -208,7 +208,8 @@ int bdattn_shard_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
  * are the merged forward results over every key the rows see, so the
  * per-call contributions of a sharded key set sum to the full gradient.
  *   q_*, k_*, v_*: as in bdattn_fwd (bf16 only).
- *   o_final: share rows x hq, o_dtype BDATTN_BF16 or BDATTN_F32.
+ *   o_final: share rows x hq, o_dtype BDATTN_BF16 or BDATTN_F32; read only
+ *          when delta_ready == 0 (to form D), otherwise not validated.
  *   lse_final: fp32 [batch][R][hq].   d_o: share rows x hq, bf16.
  *   delta: fp32 [batch][R][hq], D = rowsum(dO * O).  delta_ready == 0:
  *          computed here and stored; != 0: read as given (reuse across the
