@@ -50,7 +50,13 @@ constexpr int kRB = kBQB / 32;        // 32-row MFMA blocks per step
 constexpr int kKB = kKW / 32;         // 32-key MFMA blocks per wave
 static_assert(kBKB % kKW == 0 && kKW % 32 == 0, "whole 32-key blocks per wave");
 static_assert(kBQB == kTileRows, "one lane per row stages the per-row data; 64-row tiles");
-static_assert(kWaves >= 4, "the four per-row arrays are staged one per wave");
+// The P-waves issue every copy: the step's global -> LDS copies (32 KB)
+// take the CU's load path about 500 cycles, and a wave stalls while its
+// copies are accepted.  The S-waves' scores and exponentials lead to the
+// mid-step barrier, where the P-waves otherwise wait, so the stall belongs
+// on the P-waves.
+constexpr int kCopyWaves = kPairs;
+static_assert(kCopyWaves >= 4, "the four per-row arrays are staged one per copying wave");
 
 template <int D>
 struct __attribute__((aligned(16))) DkdvSmem {
@@ -69,21 +75,22 @@ struct __attribute__((aligned(16))) DkdvSmem {
 };
 
 // Issues the copies of one step (64 rows from compact row cq of head hb)
-// into buffer B.  Every wave copies its share of each tile.
+// into buffer B: copying wave cw (of kCopyWaves, lane offsets oc) copies
+// its share of each tile.
 template <int D>
 __device__ __forceinline__ void stage(const DkdvArgs& A, const Plan& P, int kkind, int64_t hb, int64_t cq,
-                                      int wave, int lane, const LaneOff<D>& o, DkdvSmem<D>& sm, int B) {
-  constexpr int PER = kBQB * D / 512 / kWaves;  // 1 KB blocks per wave per tile
+                                      int cw, int lane, const LaneOff<D>& oc, DkdvSmem<D>& sm, int B) {
+  constexpr int PER = kBQB * D / 512 / kCopyWaves;  // 1 KB blocks per copying wave per tile
   const int64_t base = uniform64((hb * P.nqc + cq) * D);  // natural and transposed tiles alike
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int blk = (wave + kWaves * j) * 512;  // elements
-    const int64_t e = base + (int64_t)j * kWaves * 512;
-    copy16(A.qh + e, o.dn[j & 1], &sm.q[B][blk]);
-    copy16(A.doh + e, o.dn[j & 1], &sm.dO[B][blk]);
+    const int blk = (cw + kCopyWaves * j) * 512;  // elements
+    const int64_t e = base + (int64_t)j * kCopyWaves * 512;
+    copy16(A.qh + e, oc.dn[j & 1], &sm.q[B][blk]);
+    copy16(A.doh + e, oc.dn[j & 1], &sm.dO[B][blk]);
   }
   const uint32_t lo = (uint32_t)lane * 4;
-  switch (wave) {
+  switch (cw) {
     case 0: copy4(A.lse2 + hb * P.nqc + cq, lo, &sm.lse2[B][0]); break;
     case 1: copy4(A.dc + hb * P.nqc + cq, lo, &sm.dc[B][0]); break;
     case 2: copy4(A.vis + (int64_t)(2 * kkind) * P.nqc + cq, lo, &sm.vlo[B][0]); break;
@@ -285,7 +292,9 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
   };
   auto hb_of = [&](const StepPos& p) { return (int64_t)(b * P.hq + g * P.G + p.hs); };
   auto cq_of = [&](const StepPos& p) { return (int64_t)P.q[uniform(sm.wseg[p.j])].tile0 * kBQ + row_of(p); };
-  stage<D>(A, P, K.kind, hb_of(cur), cq_of(cur), wave, lane, o, sm, 0);
+  // copy offsets of the P-waves (copying wave wave - kPairs)
+  const LaneOff<D> oc = lane_offsets<D, kCopyWaves>(S_WAVE ? 0 : wave - kPairs, lane);
+  if constexpr (!S_WAVE) stage<D>(A, P, K.kind, hb_of(cur), cq_of(cur), wave - kPairs, lane, oc, sm, 0);
   wait_copies();
   __syncthreads();
   // one step of the walk; the buffer index is a constant in each of the two
@@ -296,7 +305,7 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
     StepPos nxt = cur;
     if (more) {
       nxt = advance(cur);
-      stage<D>(A, P, K.kind, hb_of(nxt), cq_of(nxt), wave, lane, o, sm, B ^ 1);
+      if constexpr (!S_WAVE) stage<D>(A, P, K.kind, hb_of(nxt), cq_of(nxt), wave - kPairs, lane, oc, sm, B ^ 1);
     }
     if constexpr (S_WAVE) {
       // no mask when every row of the step exists and sees every key of the tile
