@@ -295,6 +295,19 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
   // copy offsets of the P-waves (copying wave wave - kPairs)
   const LaneOff<D> oc = lane_offsets<D, kCopyWaves>(S_WAVE ? 0 : wave - kPairs, lane);
   if constexpr (!S_WAVE) stage<D>(A, P, K.kind, hb_of(cur), cq_of(cur), wave - kPairs, lane, oc, sm, 0);
+  // S-waves: no mask when every row of the step exists and sees every key of
+  // the tile.  Formed for the next step at the end of the current one, so
+  // its dependent reads (walk metadata, segment table) wait under the copy
+  // wait instead of delaying the scores.
+  auto full_of = [&](const StepPos& p) {
+    const QSeg& S = P.q[uniform(sm.wseg[p.j])];
+    const int32_t r0 = row_of(p);
+    bool f = false;
+    if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= S.nrows)
+      f = row_bounds(P, S, r0).hi_clean >= kt1 && row_bounds(P, S, r0 + kBQB - 1).lo_clean <= kt1 - kvalid;
+    return f;
+  };
+  bool full_next = S_WAVE ? full_of(cur) : false;
   wait_copies();
   __syncthreads();
   // one step of the walk; the buffer index is a constant in each of the two
@@ -303,17 +316,14 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
     constexpr int B = decltype(b_c)::value;
     const bool more = t + 1 < total;
     StepPos nxt = cur;
-    if (more) {
-      nxt = advance(cur);
-      if constexpr (!S_WAVE) stage<D>(A, P, K.kind, hb_of(nxt), cq_of(nxt), wave - kPairs, lane, oc, sm, B ^ 1);
+    if constexpr (!S_WAVE) {
+      if (more) {
+        nxt = advance(cur);
+        stage<D>(A, P, K.kind, hb_of(nxt), cq_of(nxt), wave - kPairs, lane, oc, sm, B ^ 1);
+      }
     }
     if constexpr (S_WAVE) {
-      // no mask when every row of the step exists and sees every key of the tile
-      const QSeg& S = P.q[uniform(sm.wseg[cur.j])];
-      const int32_t r0 = row_of(cur);
-      bool full = false;
-      if (K.kind == KIND_CLEAN && kvalid == kBKB && r0 + kBQB <= S.nrows)
-        full = row_bounds(P, S, r0).hi_clean >= kt1 && row_bounds(P, S, r0 + kBQB - 1).lo_clean <= kt1 - kvalid;
+      const bool full = full_next;
       f16x8 pf[kRB][kKB][2];
       if (full)
         s_phase_a<D, true>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
@@ -333,6 +343,12 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
       f16x8 dsf[kRB][kKB][2];
       p_phase_ds<D>(sm, kw, lane, dcs, pacc, dsf);
       rows_contract<D>(sm.q[B], o, dsf, acc, fr);  // dK^T += Q^T dS
+    }
+    if constexpr (S_WAVE) {
+      if (more) {
+        nxt = advance(cur);
+        full_next = full_of(nxt);
+      }
     }
     wait_copies();
     __syncthreads();  // the next step's copies have landed; this step's reads are done
