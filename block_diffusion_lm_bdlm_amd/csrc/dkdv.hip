@@ -23,7 +23,7 @@
 // as fp16 rows; per-row log2 LSE, D and visible key interval) go from
 // global memory straight into LDS through the load units (global_load_lds),
 // double buffered, into unpadded tiles whose 16-byte chunks are
-// XOR-swizzled by row.  S and dP read the tiles along their rows; the
+// XOR-swizzled by row; the P-waves issue these copies (see kCopyWaves).  S and dP read the tiles along their rows; the
 // contractions over rows (dV, dK) read the same tiles across their rows
 // with the transposing LDS read, so each operand is staged once.  All
 // products run in fp16 (Q, dO, K and V come converted by the packing): the
