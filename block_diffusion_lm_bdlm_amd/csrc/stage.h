@@ -149,14 +149,6 @@ __device__ __forceinline__ void mfma_f16_agpr(f32x16& acc, const f16x8& a, const
 }
 // acc = A B (first) or acc += A B with B held in AGPRs and the result in
 // VGPRs, for operands that stay in registers for a whole walk.
-__device__ __forceinline__ f32x16 mfma_bf16_bagpr0(const bf16x8& a, const bf16x8& b) {
-  f32x16 d;
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-  return d;
-}
-__device__ __forceinline__ void mfma_bf16_bagpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
 __device__ __forceinline__ f32x16 mfma_f16_bagpr0(const f16x8& a, const f16x8& b) {
   f32x16 d;
   asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
