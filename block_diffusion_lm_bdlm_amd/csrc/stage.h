@@ -162,14 +162,31 @@ template <typename T>
 __device__ __forceinline__ void keep_in_agpr(T& x) {
   asm volatile("" : "+a"(x));
 }
-// Wait states between products whose results vector code reads next, or
-// between vector writes and products that read them (covers both).
-__device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
-// Wait states between vector writes and a product that reads them.
-__device__ __forceinline__ void mfma_settle_short() { asm volatile("s_nop 3"); }
-// Wait states before vector code may read an accumulator that a product
-// just wrote (more than a 32x32x16 product's 16 passes).
-__device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+// Wait states around inline-assembly products, which the compiler's own
+// wait-state placement cannot see.  Each is fenced by scheduling barriers
+// so that no instruction crosses it: the compiler could otherwise move a
+// vector read of a product's result (or a vector write of its operand)
+// past the wait, which nothing in the data flow forbids.
+// Between products whose results vector code reads next, or between vector
+// writes and products that read them (covers both).
+__device__ __forceinline__ void mfma_settle() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Between vector writes and a product that reads them.
+__device__ __forceinline__ void mfma_settle_short() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 3");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Before vector code may read an accumulator that a product just wrote
+// (more than a 32x32x16 product's 16 passes).
+__device__ __forceinline__ void agpr_settle() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Fragment reads kept in flight ahead of the products that consume them;
 // scheduling barriers pin this order (the compiler otherwise sinks each
