@@ -1,7 +1,11 @@
-"""Build libbdattn.so in-tree with hipcc for gfx950.
+"""Build the shared libraries in-tree with hipcc for gfx950.
+
+  libbdattn.so   BDLM attention (include/bdattn.h)
+  libbdvocab.so  streaming vocabulary loss (include/bdvocab.h), linked with
+                 hipBLASLt for its two plain GEMMs
 
 Every translation unit is compiled as HIP (the host ABI shares the planning
-functions with the kernels) and linked into one shared library next to this
+functions with the kernels) and linked into a shared library next to this
 file.  Packed-fp32 instructions are disabled for the device code.
 """
 import concurrent.futures as cf
@@ -13,8 +17,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
+VOCAB_LIB = os.path.join(HERE, "libbdvocab.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["bdattn.cpp", "fwd.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
+VOCAB_SOURCES = ["bdvocab.cpp", "vocab_rows.hip"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+VOCAB_LINK = ["-L", os.path.join(ROCM, "lib"), "-lhipblaslt", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
 # Per-file code generation options for the bf16 kernels: every matrix
 # product the compiler emits uses the VGPR form, so scores feed vector code
 # with no AGPR -> VGPR copies; the backward kernels keep their long-lived
@@ -50,17 +58,27 @@ def _compile(src):
     return obj, warn
 
 
+def _link(objs, out, extra=()):
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + list(objs) + list(extra)
+    subprocess.run(cmd, check=True, capture_output=not verbose_link[0])
+    os.replace(tmp, out)
+
+
+verbose_link = [False]
+
+
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, warn in results:
+    verbose_link[0] = verbose
+    srcs = SOURCES + VOCAB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        results = dict(zip(srcs, ex.map(_compile, srcs)))
+    for _, warn in results.values():
         if warn.strip() and verbose:
             print(warn, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + [o for o, _ in results]
-    subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    _link([results[x][0] for x in SOURCES], LIB)
+    _link([results[x][0] for x in VOCAB_SOURCES], VOCAB_LIB, VOCAB_LINK)
     return LIB
 
 

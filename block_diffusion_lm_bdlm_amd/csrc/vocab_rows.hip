@@ -1,0 +1,216 @@
+// vocab_rows.hip — the hand-written kernels of the streaming vocabulary loss
+// ([P3] Turbo-dLLM project page, "Library" section, "Vocabulary loss" rows):
+// the fused per-row pass over one chunk of fp32 logits, the gather of
+// listed hidden rows into a packed chunk, the scatter of the chunk's dh
+// rows back, and the fixed-order sum of the per-row losses.
+//
+// Per-row pass (one workgroup per row at a time, rows strided over a grid
+// sized to keep the rows in flight within the chip's caches):
+//   pass 1  one read of the row: running (max, sum of exp) per thread in
+//           the base-2 domain, one rescale per group of loads, then a
+//           workgroup merge of the (max, sum) pairs into lse;
+//   pass 2  a second read of the row: g_v = w (exp(s_v - lse) - [v == y]),
+//           rounded to bf16 and written over the first half of the same
+//           row, so the gradient GEMM reads it with twice the fp32 pitch.
+// The in-place write is safe because each group's writes land in bytes
+// that every thread of the workgroup has already read: group k reads the
+// float4 indices [kUT, (k+1)UT) and writes bf16 over the float4 indices
+// [kUT/2, (k+1)UT/2); one barrier between a group's loads and its stores
+// orders them.  The logit at the target is read before pass 2 begins.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vocab_kernels.h"
+
+namespace bdvocab {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 x = (__bf16)a;  // round to nearest even
+  const __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Merge (m, s) with (m2, s2): base-2 log-sum-exp pairs; m = -inf means empty.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  m = mn;
+}
+
+template <int T, int U>
+__global__ __launch_bounds__(T) void rows_kernel(RowsArgs a) {
+  static_assert(T % 64 == 0 && T <= 1024, "workgroup size");
+  constexpr int kWaves = T / 64;
+  __shared__ float red_m[kWaves], red_s[kWaves];
+  __shared__ float row_lse2, row_sy;
+  const int tid = threadIdx.x;
+  const int64_t n4 = a.ld / 4;  // float4 per row (ld is a multiple of 4)
+  const int64_t per_group = (int64_t)U * T;
+  const int64_t groups = (n4 + per_group - 1) / per_group;
+
+  for (int64_t r = blockIdx.x; r < a.n; r += gridDim.x) {
+    float* srow = a.s + r * a.ld;
+    const int32_t y = a.targets[r];
+    const bool valid = y >= 0 && y < a.V;
+    const float w = valid ? (a.weights ? a.weights[r] : 1.f) : 0.f;
+    if (tid == 0) row_sy = valid ? srow[y] : 0.f;
+
+    // pass 1: running base-2 max and sum of exp per thread
+    float m = -INFINITY, sum = 0.f;
+    for (int64_t g = 0; g < groups; ++g) {
+      float4 x[U];
+      float gm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = g * per_group + (int64_t)u * T + tid;
+        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (j < n4) v = reinterpret_cast<const float4*>(srow)[j];
+        const int64_t e = 4 * j;
+        x[u].x = e + 0 < a.V ? v.x * kLog2e : -INFINITY;
+        x[u].y = e + 1 < a.V ? v.y * kLog2e : -INFINITY;
+        x[u].z = e + 2 < a.V ? v.z * kLog2e : -INFINITY;
+        x[u].w = e + 3 < a.V ? v.w * kLog2e : -INFINITY;
+        gm = fmaxf(gm, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+      }
+      if (gm == -INFINITY) continue;
+      const float mn = fmaxf(m, gm);
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        acc += exp2f(x[u].x - mn) + exp2f(x[u].y - mn) + exp2f(x[u].z - mn) + exp2f(x[u].w - mn);
+      sum = sum * exp2f(m - mn) + acc;  // exp2(-inf) = 0 on the first group
+      m = mn;
+    }
+    // workgroup merge of (m, sum)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float m2 = __shfl_xor(m, off);
+      const float s2 = __shfl_xor(sum, off);
+      lse_merge(m, sum, m2, s2);
+    }
+    if ((tid & 63) == 0) {
+      red_m[tid >> 6] = m;
+      red_s[tid >> 6] = sum;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float mm = red_m[0], ss = red_s[0];
+      for (int i = 1; i < kWaves; ++i) lse_merge(mm, ss, red_m[i], red_s[i]);
+      const float lse2 = mm + log2f(ss);
+      row_lse2 = lse2;
+      const float lse = lse2 * kLn2;
+      if (a.lse) a.lse[r] = lse;
+      a.loss[r] = valid ? w * (lse - row_sy) : 0.f;
+    }
+    __syncthreads();
+    const float lse2 = row_lse2;
+
+    // pass 2: g = w (p - onehot) in bf16 over the first half of the row
+    uint2* grow = reinterpret_cast<uint2*>(srow);
+    for (int64_t g = 0; g < groups; ++g) {
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = g * per_group + (int64_t)u * T + tid;
+        if (j < n4) x[u] = reinterpret_cast<const float4*>(srow)[j];
+      }
+      __syncthreads();  // every read of this group is done before any write
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = g * per_group + (int64_t)u * T + tid;
+        if (j >= n4) continue;
+        const int64_t e = 4 * j;
+        float gv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = e + i < a.V ? exp2f(fmaf(gv[i], kLog2e, -lse2)) : 0.f;
+          if (e + i == y) p -= 1.f;
+          gv[i] = w * p;
+        }
+        grow[j] = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
+      }
+    }
+    __syncthreads();  // the next row reuses the shared slots
+  }
+}
+
+// Copy rows idx[r] of h (bf16, pitch h_stride) into a packed [n, d] chunk;
+// 16-byte pieces, d % 8 == 0.
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  const int pieces = a.d / 8;
+  const int64_t total = a.n * pieces;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / pieces;
+    const int c = (int)(i - r * pieces);
+    const int64_t src = (int64_t)a.rows[r] * a.h_stride + 8 * c;
+    reinterpret_cast<uint4*>(a.out + r * a.d)[c] = *reinterpret_cast<const uint4*>(a.h + src);
+  }
+}
+
+// Copy the packed [n, d] dh chunk (element size es = 2 or 4) to rows idx[r]
+// of dh (pitch dh_stride elements).
+__global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
+  const int pieces = a.d * a.es / 16;
+  const int64_t total = a.n * pieces;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / pieces;
+    const int c = (int)(i - r * pieces);
+    const int64_t dst = ((int64_t)a.rows[r] * a.dh_stride) * a.es + 16 * (int64_t)c;
+    *reinterpret_cast<uint4*>(a.dh + dst) = reinterpret_cast<const uint4*>(a.in + r * (int64_t)a.d * a.es)[c];
+  }
+}
+
+// Sum of n per-row losses in a fixed order: thread t adds rows t, t + 1024,
+// ... in double, then a fixed tree over the threads.
+__global__ __launch_bounds__(1024) void loss_sum_kernel(const float* loss, int64_t n, float* out) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += (double)loss[i];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = (float)part[0];
+}
+
+}  // namespace
+
+hipError_t launch_rows(const RowsArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  const int grid = (int)(a.n < kRowsInFlight ? a.n : kRowsInFlight);
+  hipLaunchKernelGGL((rows_kernel<kRowThreads, kRowGroup>), dim3(grid), dim3(kRowThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  const int64_t total = a.n * (a.d / 8);
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  const int64_t total = a.n * (a.d * a.es / 16);
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(scatter_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_sum(const float* loss, int64_t n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(1024), 0, s, loss, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace bdvocab

@@ -1,0 +1,118 @@
+/*
+ * bdvocab.h — C ABI of libbdvocab: the streaming vocabulary loss of BDLM
+ * training on AMD MI355X (gfx950).
+ *
+ * Source (cited by page title and section):
+ *  [P3] "Block Parallelism for Efficient Distributed Long-Context Diffusion
+ *       Language Model Training" (Turbo-dLLM project page), "Library"
+ *       section, tables "Speculative Decoding Optimizations" and "Block
+ *       Diffusion Optimizations", row "Vocabulary loss": rows are streamed
+ *       through the frozen LM head in token chunks, with projection and
+ *       cross-entropy done per chunk, so the logits of the whole sequence
+ *       are never held.
+ *
+ * What is computed.  For the R rows that carry the loss (the masked
+ * positions of the corrupted copy, chosen by the caller), with hidden row
+ * h_r (length d), target y_r and weight w_r, and the frozen head W [V, d]:
+ *   s_r    = h_r W^T                         (the row's V logits)
+ *   lse_r  = log sum_v exp(s_rv)
+ *   loss_r = w_r (lse_r - s_r[y_r])
+ *   dh_r   = w_r (softmax(s_r) - e_{y_r}) W   (gradient of loss_r wrt h_r)
+ * The head is frozen: no gradient for W is formed.  A row whose target is
+ * outside [0, V) is ignored: loss_r = 0, dh_r = 0 (lse_r is still written).
+ *
+ * How.  Rows go in chunks of C.  Per chunk: the chunk's logits in fp32
+ * (a plain library GEMM, bf16 inputs, fp32 accumulation) into the
+ * workspace; one fused pass per row forms lse, the loss and the logit
+ * gradient, written in bf16 over the same workspace rows; a second library
+ * GEMM forms dh.  Device memory for logits is C * V * 4 bytes, never R * V.
+ *
+ * Conventions.
+ *   - Device buffers are caller-owned; the library allocates no device
+ *     memory (the GEMM library's handle is created once per device).
+ *     Scratch comes from `workspace` (size from bdvocab_workspace_bytes).
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL =
+ *     the null stream); buffers must stay valid until it completes.  Calls
+ *     sharing a workspace must not overlap.
+ *   - Return value: BDVOCAB_OK or a negative bdvocab_status.  Argument
+ *     errors are found on the host before anything is enqueued; device
+ *     contents (targets, row indices) are not checked on the host.
+ */
+#ifndef BDVOCAB_H
+#define BDVOCAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BDVOCAB_OK = 0,
+  BDVOCAB_EINVAL = -1,     /* bad argument (sizes, strides, missing buffer) */
+  BDVOCAB_ENOTSUP = -2,    /* valid but unsupported (hidden size not a multiple of 8, dtype) */
+  BDVOCAB_EHIP = -3,       /* a HIP runtime call failed */
+  BDVOCAB_EWORKSPACE = -4, /* workspace too small or misaligned */
+  BDVOCAB_EBLAS = -5       /* the GEMM library refused or failed */
+} bdvocab_status;
+
+typedef enum { BDVOCAB_BF16 = 0, BDVOCAB_F32 = 1 } bdvocab_dtype;
+
+typedef struct {
+  int64_t n_rows;   /* R >= 0: rows that carry the loss */
+  int32_t vocab;    /* V >= 1 */
+  int32_t hidden;   /* d >= 8, multiple of 8 */
+  int32_t chunk;    /* C: rows per chunk, >= 1; 0 picks the default (8192) */
+  int32_t dh_dtype; /* BDVOCAB_BF16 or BDVOCAB_F32 */
+} bdvocab_problem;
+
+/* Bytes of device workspace bdvocab_loss needs for `problem` (256-byte
+ * aligned base required).  `row_list` != 0 when the call passes a row index
+ * list (adds the gathered chunk of hidden rows and of dh).  Returns 0 for an
+ * invalid problem. */
+size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list);
+
+/* Loss, lse and dh of the R loss rows.
+ *   h        bf16, device.  Row r is read at h + idx_r * h_stride elements,
+ *            idx_r = rows[r] when `rows` is given, else r; the d values of a
+ *            row are contiguous.  h_stride >= d.
+ *   w_head   bf16 [V, d] row-major, contiguous, device.
+ *   rows     int32 [R] device, or NULL.  Distinct, each in [0, 2^31); the
+ *            caller guarantees h and dh hold row idx_r (not checked).
+ *   targets  int32 [R] device.
+ *   weights  fp32 [R] device, or NULL for weight 1.
+ *   lse      fp32 [R] device, or NULL.
+ *   loss     fp32 [R] device (per-row weighted loss), required.
+ *   loss_sum fp32 device scalar, or NULL: sum of loss over the rows, in a
+ *            fixed order (deterministic).
+ *   dh       device, dtype problem->dh_dtype, or NULL to skip the gradient.
+ *            Row idx_r of dh (at dh + idx_r * dh_stride elements) is
+ *            written for every r; other rows are not touched.  dh_stride
+ *            >= d.
+ *   workspace / ws_bytes: at least bdvocab_workspace_bytes(problem,
+ *            rows != NULL); the contents need not be initialised.
+ * R = 0 enqueues only the zeroing of loss_sum. */
+int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride,
+                 const void* w_head, const int32_t* rows, const int32_t* targets,
+                 const float* weights, float* lse, float* loss, float* loss_sum,
+                 void* dh, int64_t dh_stride, void* workspace, size_t ws_bytes,
+                 void* hip_stream);
+
+/* Static text for a bdvocab_status value. */
+const char* bdvocab_status_string(int status);
+
+/* Kernel timing for measurement: when enabled (nonzero), every launch of
+ * bdvocab_loss is bracketed by HIP events on its stream, per kind:
+ * "logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum".
+ * bdvocab_profile_read synchronises the recorded events, writes up to `cap`
+ * (name, launch count, total milliseconds) entries for the kinds that ran,
+ * sets *n to their number and clears the record. */
+int bdvocab_profile_enable(int enable);
+int bdvocab_profile_read(const char** names, int64_t* counts, double* ms, int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDVOCAB_H */

@@ -1,0 +1,98 @@
+"""Host-side contract of libbdvocab, checked without a GPU: the library
+loads and exports every entry point of include/bdvocab.h, the workspace
+size follows its stated layout, and invalid arguments are rejected before
+any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_diffusion_lm_bdlm_amd import bdvocab as BV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "bdvocab.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(bdvocab_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_entry_points()
+    assert len(names) == 5
+    lib = C.CDLL(BV.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(BV.EXPORTS)
+
+
+def _up(x, a=256):
+    return (x + a - 1) // a * a
+
+
+@pytest.mark.parametrize("R,V,d,chunk,dt,rows", [(32768, 131072, 5120, 0, 0, True), (300, 5000, 256, 128, 1, False),
+                                                 (5, 7, 8, 0, 0, True), (0, 10, 8, 0, 0, False)])
+def test_workspace_layout(R, V, d, chunk, dt, rows):
+    c = min(chunk if chunk > 0 else 8192, max(R, 1))
+    ld = (V + 63) // 64 * 64
+    es = 4 if dt == BV.BDVOCAB_F32 else 2
+    want = _up(c * ld * 4)
+    if rows:
+        want += _up(c * d * 2) + _up(c * d * es)
+    want += 64 << 20
+    assert BV.bdvocab_workspace_bytes(BV.problem(R, V, d, chunk, dt), rows) == want
+
+
+def _status(*a):
+    try:
+        BV.bdvocab_loss(*a, stream=0)
+    except BV.BdvocabError as e:
+        return e.status
+    return BV.BDVOCAB_OK
+
+
+class _Fake:
+    """Stands in for a device buffer: an address that is never dereferenced
+    because every call below is rejected (or does nothing) on the host."""
+
+    def __init__(self, addr, nbytes=0):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def test_invalid_arguments_rejected_on_host():
+    for bad in [BV.problem(-1, 10, 8), BV.problem(1, 0, 8), BV.problem(1, 10, 0), BV.problem(1, 10, 8, -1)]:
+        assert BV.bdvocab_workspace_bytes(bad, False) == 0
+        assert _status(bad, None, 8, None, None, None, None, None, None, None, None, 0, None) == BV.BDVOCAB_EINVAL
+    for bad in [BV.problem(4, 10, 12), BV.problem(4, 10, 4), BV.problem(4, 10, 8, 0, 2)]:
+        assert BV.bdvocab_workspace_bytes(bad, False) == 0
+        assert _status(bad, None, 8, None, None, None, None, None, None, None, None, 0, None) == BV.BDVOCAB_ENOTSUP
+    p = BV.problem(4, 100, 64)
+    ws_need = BV.bdvocab_workspace_bytes(p, False)
+    h, w, y, loss, ws = _Fake(4096), _Fake(8192), _Fake(12288), _Fake(16384), _Fake(1 << 20, ws_need)
+    assert _status(p, None, 64, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL   # no h
+    assert _status(p, h, 64, w, None, None, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL  # no targets
+    assert _status(p, h, 64, w, None, y, None, None, None, None, None, 0, ws) == BV.BDVOCAB_EINVAL     # no loss
+    assert _status(p, h, 32, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL     # stride < d
+    assert _status(p, h, 68, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL     # stride % 8
+    assert _status(p, _Fake(4098), 64, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, _Fake(20480), 60, ws) == BV.BDVOCAB_EINVAL
+    small = _Fake(1 << 20, ws_need - 1)
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, small) == BV.BDVOCAB_EWORKSPACE
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, _Fake((1 << 20) + 16, ws_need)) \
+        == BV.BDVOCAB_EWORKSPACE
+    # a row list needs the larger workspace
+    assert _status(p, h, 64, w, _Fake(24576), y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EWORKSPACE
+    # no rows and no loss sum: nothing to do, no HIP call
+    assert _status(BV.problem(0, 100, 64), None, 64, None, None, None, None, None, None, None, None, 0, None) \
+        == BV.BDVOCAB_OK
+    assert BV.bdvocab_status_string(BV.BDVOCAB_EBLAS).startswith("GEMM library")
