@@ -31,6 +31,10 @@ WORKLOADS = {
     "bdlm_L8K_M32_b2_h16kv8_d128": (2, 8192, 32, 16, 8, 128),
 }
 DEFAULT = "bdlm_L64K_M32_h40kv8_d128"
+VOCAB_WORKLOADS = {
+    # name: (L corrupted positions, block size M, hidden d, vocabulary V)
+    "vocab_L64K_M32_d5120_V131072": (65536, 32, 5120, 131072),
+}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -257,12 +261,127 @@ def report_all(reps=3):
                           "kernels_ms": {n: round(t, 4) for n, t in kern.items()}}), flush=True)
 
 
+def vocab_cpu_baseline(h, W, rows, y, wt, nrows, seed=0):
+    """Oracle (fp64 CPU) on a bounded sample of the vocabulary-loss workload:
+    loss, lse and dh of `nrows` seeded loss rows against the full head."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import vocab as ov
+    rng = np.random.default_rng(seed)
+    pick = np.sort(rng.choice(rows.numel(), size=min(nrows, rows.numel()), replace=False))
+    hs = h[rows.to(h.device)[pick].long()].float().cpu().numpy()
+    Wh = W.float().cpu().numpy()
+    t0 = time.perf_counter()
+    ov.vocab_loss(hs, Wh, y.cpu().numpy()[pick], wt.cpu().numpy()[pick])
+    dt = time.perf_counter() - t0
+    cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"value": round(len(pick) / dt, 3), "unit": "loss rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 lse, loss and dh of {len(pick)} seeded loss rows against the full "
+                      f"{W.shape[0]} x {W.shape[1]} head (numpy BLAS); {dt:.1f} s"}
+
+
+def bench_vocab(args):
+    """Streaming vocabulary loss: the masked positions of L corrupted
+    positions (per-block ratio t ~ U(0, 1)) go through the frozen head in
+    chunks of 8192 rows; one step = loss, lse, loss sum and dh of every loss
+    row.  Useful FLOPs 4 R V d (logits GEMM + gradient GEMM)."""
+    import torch
+
+    from block_diffusion_lm_bdlm_amd import bdvocab as BV
+    from block_diffusion_lm_bdlm_amd import synth
+
+    L, M, d, V = VOCAB_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    seed = synth.SEED_BASE + 3
+    print(f"[bench] generating inputs for {args.workload}", file=sys.stderr, flush=True)
+    rows = synth.masked_rows(seed, L, M)
+    R = int(rows.numel())
+    h, W, y, wt = synth.vocab_inputs(seed, L, d, V, R=R, device=dev)
+    rows_d = rows.to(dev)
+    vl = BV.VocabLoss(R, V, d, row_list=True, device=dev)
+    dh = torch.zeros((L, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(R, dtype=torch.float32, device=dev)
+    loss = torch.empty(R, dtype=torch.float32, device=dev)
+    loss_sum = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def step():
+        vl(h, W, y, weights=wt, rows=rows_d, dh=dh, lse=lse, loss=loss, loss_sum=loss_sum)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    BV.bdvocab_profile_read()
+    BV.bdvocab_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    BV.bdvocab_profile_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = BV.bdvocab_profile_read()
+    print(f"[bench] {args.steps} steps, {ms:.2f} ms/step; kernels: "
+          + ", ".join(f"{n} {c}x {t / c:.3f} ms" for n, (c, t) in sorted(prof.items(), key=lambda x: -x[1][1])),
+          file=sys.stderr, flush=True)
+    useful = 4.0 * R * V * d
+    tflops = useful / (ms * 1e-3) / 1e12
+    chunk = min(8192, R)
+    n_chunks = (R + chunk - 1) // chunk
+    gemm_flops = 2.0 * chunk * V * d  # per launch of a full chunk (the ragged last one is smaller)
+    dom_name, (dom_cnt, dom_ms) = max(((k_, v_) for k_, v_ in prof.items() if k_.endswith("gemm")),
+                                      key=lambda kv_: kv_[1][1])
+    dom_flops = 2.0 * R * V * d * args.steps / dom_cnt  # average work per launch
+    dom_avg = dom_ms / dom_cnt
+    ach = dom_flops / (dom_avg * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom_name),
+            "avg_ms": round(dom_avg, 3), "library": "hipBLASLt"}
+    rc, rms = prof["rows"]
+    rows_bytes = 6.0 * R * V * args.steps / rc  # fp32 logits read once + bf16 gradient written, per launch
+    rach = rows_bytes / (rms / rc * 1e-3) / 1e9
+    roof_rows = {"bound": "hbm", "kernel": "rows", "achieved": round(rach, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(rach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("rows_kernel"),
+                 "avg_ms": round(rms / rc, 3)}
+    cpu = None
+    if args.cpu_rows > 0:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        cpu = vocab_cpu_baseline(h, W, rows, y, wt, min(args.cpu_rows, 64))
+    out = {
+        "metric": "vocabulary loss rows/s through the frozen head, loss + dh (1 GPU)",
+        "value": round(R / (ms * 1e-3), 1),
+        "unit": "loss rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) hidden rows, N(0, 9/d) head, uniform targets, seeded",
+        "config": {"workload": args.workload, "L": L, "M": M, "loss_rows": R, "hidden": d, "vocab": V,
+                   "chunk": chunk, "chunks": n_chunks, "parallelism": "single GPU"},
+        "useful_tflops": round(tflops, 2),
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "gemm_flop_per_full_chunk": gemm_flops,
+        "logits_bytes_per_chunk": chunk * ((V + 63) // 64 * 64) * 4,
+        "kernels": {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof.items()},
+        "roofline": roof,
+        "roofline_rows": roof_rows,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS) + sorted(VOCAB_WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (counter calibration) and exit")
@@ -279,6 +398,10 @@ def main():
         print("bench.py measures one GPU's share of the hot path; runs on more than one GPU are not "
               "part of this build (see DESIGN.md, 'How the path would shard').", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in VOCAB_WORKLOADS:
+        bench_vocab(args)
+        return
 
     import torch
 

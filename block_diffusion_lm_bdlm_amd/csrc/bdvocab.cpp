@@ -14,11 +14,21 @@
 // In the GEMM library's column-major terms a row-major [r, c] matrix with
 // pitch p is a c x r matrix with leading dimension p, so the logits GEMM is
 // S^T (V x n) = op_T(W^T as d x V) * (H^T as d x n) and the gradient GEMM
-// is dH^T (d x n) = (W^T as d x V) * (G^T as V x n).
+// is dH^T (d x n) = op_T(Wt^T as V x d) * (G^T as V x n), with Wt the
+// head transposed to [d, V] once per call (a hand-written LDS-tiled copy
+// into the workspace): both products then read their two operands along
+// the contraction, the layout the library runs fastest (measured: the
+// gradient GEMM on W itself, not transposed, was 25-30% slower).
+// Algorithm choice: on the first use of a shape, the library's top
+// candidates are timed on the call's stream (which synchronises that first
+// call) and the fastest is kept for the process; BDVOCAB_TUNE=0 in the
+// environment keeps the library's first candidate instead.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -35,6 +45,7 @@ constexpr int32_t kDefaultChunk = 8192;
 constexpr size_t kBlasWs = size_t(64) << 20;  // GEMM library workspace
 constexpr size_t kAlign = 256;
 constexpr int kMaxDevices = 64;
+constexpr int kCandidates = 8;  // GEMM algorithms timed on a shape's first use
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -44,7 +55,7 @@ int64_t logit_pitch(int32_t V) { return ((int64_t)V + 63) / 64 * 64; }
 struct Layout {
   int64_t chunk = 0;
   int64_t ld = 0;
-  size_t s_off = 0, hc_off = 0, dhc_off = 0, blas_off = 0, total = 0;
+  size_t s_off = 0, wt_off = 0, hc_off = 0, dhc_off = 0, blas_off = 0, total = 0;
 };
 
 int check_problem(const bdvocab_problem* p) {
@@ -65,6 +76,8 @@ Layout layout(const bdvocab_problem& p, bool row_list) {
   size_t off = 0;
   L.s_off = off;
   off = round_up(off + (size_t)c * (size_t)L.ld * 4, kAlign);
+  L.wt_off = off;  // the head transposed, [d, ld] bf16
+  off = round_up(off + (size_t)p.hidden * (size_t)L.ld * 2, kAlign);
   if (row_list) {
     L.hc_off = off;
     off = round_up(off + (size_t)c * (size_t)p.hidden * 2, kAlign);
@@ -78,8 +91,9 @@ Layout layout(const bdvocab_problem& p, bool row_list) {
 }
 
 // ------------------------------------------------------------------ profiling
-enum Kind { K_LOGITS, K_ROWS, K_GRAD, K_GATHER, K_SCATTER, K_SUM, K_COUNT };
-const char* kKindNames[K_COUNT] = {"logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum"};
+enum Kind { K_LOGITS, K_ROWS, K_GRAD, K_GATHER, K_SCATTER, K_SUM, K_TRANSPOSE, K_COUNT };
+const char* kKindNames[K_COUNT] = {"logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum",
+                                   "transpose"};
 
 struct Prof {
   std::mutex mu;
@@ -189,11 +203,45 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
       if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return BDVOCAB_EBLAS;
       uint64_t cap = kBlasWs;
       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap));
+      hipblasLtMatmulHeuristicResult_t cand[kCandidates];
       int found = 0;
       const hipblasStatus_t st =
-          hipblasLtMatmulAlgoGetHeuristic(h, g.op, g.a, g.b, g.d, g.d, pref, 1, &best, &found);
+          hipblasLtMatmulAlgoGetHeuristic(h, g.op, g.a, g.b, g.d, g.d, pref, kCandidates, cand, &found);
       hipblasLtMatmulPreferenceDestroy(pref);
-      if (st != HIPBLAS_STATUS_SUCCESS || found < 1 || best.workspaceSize > kBlasWs) return BDVOCAB_EBLAS;
+      if (st != HIPBLAS_STATUS_SUCCESS || found < 1) return BDVOCAB_EBLAS;
+      int pick = -1;
+      const char* env = std::getenv("BDVOCAB_TUNE");
+      const bool tune = found > 1 && !(env && std::strcmp(env, "0") == 0);
+      if (tune) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return BDVOCAB_EHIP;
+        float best_ms = 0.f;
+        const float one = 1.f, zero = 0.f;
+        for (int i = 0; i < found; ++i) {
+          if (cand[i].state != HIPBLAS_STATUS_SUCCESS || cand[i].workspaceSize > kBlasWs) continue;
+          // one untimed run, then two timed ones
+          bool ok = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, &zero, D, g.d, D, g.d, &cand[i].algo, ws,
+                                    kBlasWs, s) == HIPBLAS_STATUS_SUCCESS;
+          ok = ok && hipEventRecord(e0, s) == hipSuccess;
+          for (int r = 0; ok && r < 2; ++r)
+            ok = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, &zero, D, g.d, D, g.d, &cand[i].algo, ws, kBlasWs,
+                                 s) == HIPBLAS_STATUS_SUCCESS;
+          ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+          float ms = 0.f;
+          ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+          if (ok && (pick < 0 || ms < best_ms)) {
+            pick = i;
+            best_ms = ms;
+          }
+        }
+        hipEventDestroy(e0);
+        hipEventDestroy(e1);
+      } else {
+        for (int i = 0; i < found && pick < 0; ++i)
+          if (cand[i].state == HIPBLAS_STATUS_SUCCESS && cand[i].workspaceSize <= kBlasWs) pick = i;
+      }
+      if (pick < 0) return BDVOCAB_EBLAS;
+      best = cand[pick];
       g_blas.algos[key] = best;
     }
   }
@@ -237,7 +285,13 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
     float* S = reinterpret_cast<float*>(ws + L.s_off);
     uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc_off);
     uint8_t* dhc = ws + L.dhc_off;
+    uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.wt_off);
     void* blas_ws = ws + L.blas_off;
+    if (dh) {
+      const TransposeArgs ta{static_cast<const uint16_t*>(w_head), p.vocab, (int32_t)d, wt, L.ld};
+      const int rc = timed(K_TRANSPOSE, s, [&] { return hip_rc(launch_transpose(ta, s)); });
+      if (rc != BDVOCAB_OK) return rc;
+    }
     const hipDataType dt = p.dh_dtype == BDVOCAB_F32 ? HIP_R_32F : HIP_R_16BF;
     for (int64_t c0 = 0; c0 < R; c0 += L.chunk) {
       const int64_t n = std::min<int64_t>(L.chunk, R - c0);
@@ -261,7 +315,7 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
       if (!dh) continue;
       void* D = rows ? static_cast<void*>(dhc) : static_cast<void*>(static_cast<uint8_t*>(dh) + c0 * dh_stride * es);
       const int64_t ldd = rows ? d : dh_stride;
-      rc = timed(K_GRAD, s, [&] { return gemm(false, false, d, n, p.vocab, w_head, d, S, 2 * L.ld, D, dt, ldd, blas_ws, s); });
+      rc = timed(K_GRAD, s, [&] { return gemm(true, false, d, n, p.vocab, wt, L.ld, S, 2 * L.ld, D, dt, ldd, blas_ws, s); });
       if (rc != BDVOCAB_OK) return rc;
       if (rows) {
         const ScatterArgs sa{dhc, n, (int32_t)d, es, rows + c0, static_cast<uint8_t*>(dh), dh_stride};

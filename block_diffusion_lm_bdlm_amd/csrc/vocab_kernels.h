@@ -7,10 +7,20 @@
 namespace bdvocab {
 
 // Per-row pass: workgroup size, float4 loads per thread between barriers,
-// and the grid cap (rows in flight at once, strided loop beyond).
-constexpr int kRowThreads = 512;
-constexpr int kRowGroup = 8;
-constexpr int kRowsInFlight = 512;
+// and the grid cap (rows in flight at once, strided loop beyond).  The
+// macros only serve launch-shape sweeps.
+#ifndef BDVOCAB_ROW_THREADS
+#define BDVOCAB_ROW_THREADS 1024
+#endif
+#ifndef BDVOCAB_ROW_GROUP
+#define BDVOCAB_ROW_GROUP 4
+#endif
+#ifndef BDVOCAB_ROWS_IN_FLIGHT
+#define BDVOCAB_ROWS_IN_FLIGHT 256
+#endif
+constexpr int kRowThreads = BDVOCAB_ROW_THREADS;
+constexpr int kRowGroup = BDVOCAB_ROW_GROUP;
+constexpr int kRowsInFlight = BDVOCAB_ROWS_IN_FLIGHT;
 
 struct RowsArgs {
   float* s;               // [n, ld] fp32 logits in; bf16 gradient out (pitch 2*ld bf16)
@@ -42,9 +52,18 @@ struct ScatterArgs {
   int64_t dh_stride;
 };
 
+struct TransposeArgs {
+  const uint16_t* w;      // [V, d] bf16, pitch d
+  int64_t V;
+  int32_t d;              // multiple of 8
+  uint16_t* wt;           // [d, ldt] bf16
+  int64_t ldt;            // multiple of 8, >= V
+};
+
 hipError_t launch_rows(const RowsArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
 hipError_t launch_loss_sum(const float* loss, int64_t n, float* out, hipStream_t s);
 
 }  // namespace bdvocab

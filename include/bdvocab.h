@@ -25,7 +25,11 @@
  * (a plain library GEMM, bf16 inputs, fp32 accumulation) into the
  * workspace; one fused pass per row forms lse, the loss and the logit
  * gradient, written in bf16 over the same workspace rows; a second library
- * GEMM forms dh.  Device memory for logits is C * V * 4 bytes, never R * V.
+ * GEMM forms dh from a transposed copy of the head made once per call.
+ * Device memory for logits is C * V * 4 bytes, never R * V.  The first call
+ * of a shape times the GEMM library's candidate algorithms on the call's
+ * stream (synchronising that call) and keeps the fastest; BDVOCAB_TUNE=0
+ * in the environment keeps the library's first candidate.
  *
  * Conventions.
  *   - Device buffers are caller-owned; the library allocates no device
@@ -68,7 +72,8 @@ typedef struct {
 } bdvocab_problem;
 
 /* Bytes of device workspace bdvocab_loss needs for `problem` (256-byte
- * aligned base required).  `row_list` != 0 when the call passes a row index
+ * aligned base required): the chunk's logits, the transposed head, and the
+ * GEMM library's 64 MiB.  `row_list` != 0 when the call passes a row index
  * list (adds the gathered chunk of hidden rows and of dh).  Returns 0 for an
  * invalid problem. */
 size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list);
@@ -104,7 +109,8 @@ const char* bdvocab_status_string(int status);
 
 /* Kernel timing for measurement: when enabled (nonzero), every launch of
  * bdvocab_loss is bracketed by HIP events on its stream, per kind:
- * "logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum".
+ * "logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum",
+ * "transpose".
  * bdvocab_profile_read synchronises the recorded events, writes up to `cap`
  * (name, launch count, total milliseconds) entries for the kinds that ran,
  * sets *n to their number and clears the record. */

@@ -37,7 +37,7 @@ def test_workspace_layout(R, V, d, chunk, dt, rows):
     c = min(chunk if chunk > 0 else 8192, max(R, 1))
     ld = (V + 63) // 64 * 64
     es = 4 if dt == BV.BDVOCAB_F32 else 2
-    want = _up(c * ld * 4)
+    want = _up(c * ld * 4) + _up(d * ld * 2)
     if rows:
         want += _up(c * d * 2) + _up(c * d * es)
     want += 64 << 20
