@@ -18,6 +18,13 @@ namespace bdvocab {
 #ifndef BDVOCAB_ROWS_IN_FLIGHT
 #define BDVOCAB_ROWS_IN_FLIGHT 256
 #endif
+// Single-read pass: workgroup size, float4 loads per thread per sub-block,
+// the largest sub-block count (logits per row up to threads x loads x 4 x
+// that count) and the grid cap; one workgroup per CU fits its registers.
+constexpr int kOnChipThreads = 512;
+constexpr int kOnChipLoads = 8;
+constexpr int kOnChipSubMax = 8;
+constexpr int kOnChipInFlight = 256;
 constexpr int kRowThreads = BDVOCAB_ROW_THREADS;
 constexpr int kRowGroup = BDVOCAB_ROW_GROUP;
 constexpr int kRowsInFlight = BDVOCAB_ROWS_IN_FLIGHT;

@@ -82,7 +82,9 @@ def _check(res):
 
 # (seed, T, R, V, d, chunk, row_list, dh_dtype): several chunks with a ragged
 # last one, vocabularies that are not multiples of the row pitch, of 4, or
-# smaller than one workgroup's loads, and both dh dtypes.
+# smaller than one workgroup's loads, both dh dtypes, and every storage
+# split of the single-read row kernel (1-4 register sub-blocks, 1-4 LDS
+# sub-blocks) plus the two-pass kernel above 131,072 logits.
 CASES = [
     (1, 300, 300, 5000, 256, 128, False, 0),
     (2, 700, 257, 1001, 64, 64, True, 1),
@@ -91,6 +93,8 @@ CASES = [
     (5, 400, 100, 32771, 128, 37, True, 0),
     (6, 96, 96, 70000, 80, 40, False, 0),
     (7, 33, 33, 3, 16, 8, True, 1),
+    (8, 48, 48, 140000, 64, 16, False, 0),   # above the single-read capacity: the two-pass kernel
+    (9, 64, 40, 131072, 64, 0, True, 1),     # the largest single-read row (register + LDS storage)
 ]
 
 
