@@ -131,3 +131,35 @@ def test_ignored_targets():
     _, loss_k, dh_k = ov.vocab_loss(h[keep], W, y[keep], w[keep])
     np.testing.assert_array_equal(loss[keep], loss_k)
     np.testing.assert_allclose(dh[keep], dh_k, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- head gradient
+@pytest.mark.parametrize("R,d,V,scale", [(13, 24, 300, 3.0), (3, 7, 5, 1.0)])
+def test_head_grad_matches_torch_autograd(R, d, V, scale):
+    h, W, y, w = _rand(20 + R, R, d, V, scale)
+    dW = ov.vocab_head_grad(h, W, y, w)
+    th = torch.tensor(h, dtype=torch.float64)
+    tw = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    ce = torch.nn.functional.cross_entropy(torch.nn.functional.linear(th, tw), torch.tensor(y), reduction="none")
+    (ce * torch.tensor(w)).sum().backward()
+    np.testing.assert_allclose(dW, tw.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_head_grad_by_finite_differences_and_vocab_sum():
+    h, W, y, w = _rand(7, 4, 5, 9, scale=2.0)
+    y = y.copy()
+    y[2] = -1  # an ignored row contributes nothing
+    dW = ov.vocab_head_grad(h, W, y, w)
+    eps = 1e-6
+    for v in (0, 3, 8):
+        for j in (0, 4):
+            Wp = W.copy()
+            Wm = W.copy()
+            Wp[v, j] += eps
+            Wm[v, j] -= eps
+            num = (ov.vocab_loss(h, Wp, y, w)[1].sum() - ov.vocab_loss(h, Wm, y, w)[1].sum()) / (2 * eps)
+            assert num == pytest.approx(dW[v, j], rel=1e-6, abs=1e-9)
+    # sum over the vocabulary of g_r is w_r (1 - 1) = 0, so dW sums to zero over v
+    assert np.abs(dW.sum(axis=0)).max() < 1e-12
+    keep = [0, 1, 3]
+    np.testing.assert_allclose(dW, ov.vocab_head_grad(h[keep], W, y[keep], w[keep]), rtol=1e-13, atol=1e-15)
