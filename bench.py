@@ -282,9 +282,11 @@ def vocab_cpu_baseline(h, W, rows, y, wt, nrows, seed=0):
 
 def bench_vocab(args):
     """Streaming vocabulary loss: the masked positions of L corrupted
-    positions (per-block ratio t ~ U(0, 1)) go through the frozen head in
-    chunks of 8192 rows; one step = loss, lse, loss sum and dh of every loss
-    row.  Useful FLOPs 4 R V d (logits GEMM + gradient GEMM)."""
+    positions (per-block ratio t ~ U(0, 1)) go through the head in chunks of
+    8192 rows; one step = loss, lse, loss sum and dh of every loss row
+    (frozen head; useful FLOPs 4 R V d: logits GEMM + gradient GEMM).  The
+    line also times the step with the head trained (dW cleared and
+    accumulated; 6 R V d) under "with_head_grad"."""
     import torch
 
     from block_diffusion_lm_bdlm_amd import bdvocab as BV
@@ -343,8 +345,34 @@ def bench_vocab(args):
     rows_bytes = 6.0 * R * V * args.steps / rc  # fp32 logits read once + bf16 gradient written, per launch
     rach = rows_bytes / (rms / rc * 1e-3) / 1e9
     roof_rows = {"bound": "hbm", "kernel": "rows", "achieved": round(rach, 1), "peak": PEAK_HBM_GBS,
-                 "unit": "GB/s", "frac": round(rach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("rows_kernel"),
+                 "unit": "GB/s", "frac": round(rach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("vocab_rows"),
                  "avg_ms": round(rms / rc, 3)}
+    # the same step with the head trained: dW cleared, then accumulated per chunk
+    dw = torch.zeros((V, d), dtype=torch.float32, device=dev)
+
+    def step_dw():
+        dw.zero_()
+        vl(h, W, y, weights=wt, rows=rows_d, dh=dh, lse=lse, loss=loss, loss_sum=loss_sum, dw=dw)
+
+    for _ in range(args.warmup):
+        step_dw()
+    torch.cuda.synchronize()
+    BV.bdvocab_profile_enable(True)
+    e0.record()
+    for _ in range(args.steps):
+        step_dw()
+    e1.record()
+    torch.cuda.synchronize()
+    BV.bdvocab_profile_enable(False)
+    ms_dw = e0.elapsed_time(e1) / args.steps
+    prof_dw = BV.bdvocab_profile_read()
+    print(f"[bench] with head gradient: {ms_dw:.2f} ms/step; kernels: "
+          + ", ".join(f"{n} {c}x {t / c:.3f} ms" for n, (c, t) in sorted(prof_dw.items(), key=lambda x: -x[1][1])),
+          file=sys.stderr, flush=True)
+    with_dw = {"ms_per_step": round(ms_dw, 3), "loss_rows_per_s": round(R / (ms_dw * 1e-3), 1),
+               "useful_tflops": round(6.0 * R * V * d / (ms_dw * 1e-3) / 1e12, 2),
+               "kernels": {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof_dw.items()}}
+    del dw
     cpu = None
     if args.cpu_rows > 0:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
@@ -371,6 +399,7 @@ def bench_vocab(args):
         "kernels": {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof.items()},
         "roofline": roof,
         "roofline_rows": roof_rows,
+        "with_head_grad": with_dw,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -42,7 +42,7 @@ def lib():
     vp, i64, i32, P = C.c_void_p, C.c_int64, C.c_int32, C.POINTER
     L.bdvocab_workspace_bytes.argtypes = [P(Problem), C.c_int]
     L.bdvocab_workspace_bytes.restype = C.c_size_t
-    L.bdvocab_loss.argtypes = [P(Problem), vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, C.c_size_t, vp]
+    L.bdvocab_loss.argtypes = [P(Problem), vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, C.c_size_t, vp]
     L.bdvocab_loss.restype = C.c_int
     L.bdvocab_status_string.argtypes = [C.c_int]
     L.bdvocab_status_string.restype = C.c_char_p
@@ -82,12 +82,12 @@ def bdvocab_workspace_bytes(prob, row_list):
     return int(lib().bdvocab_workspace_bytes(C.byref(prob), 1 if row_list else 0))
 
 
-def bdvocab_loss(prob, h, h_stride, w_head, rows, targets, weights, lse, loss, loss_sum, dh, dh_stride, workspace,
-                 stream=None):
+def bdvocab_loss(prob, h, h_stride, w_head, rows, targets, weights, lse, loss, loss_sum, dh, dh_stride, dw,
+                 workspace, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bdvocab_loss(C.byref(prob), _p(h), int(h_stride), _p(w_head), _p(rows), _p(targets), _p(weights),
-                              _p(lse), _p(loss), _p(loss_sum), _p(dh), int(dh_stride), _p(workspace), ws_bytes,
-                              _stream(stream)), "bdvocab_loss")
+                              _p(lse), _p(loss), _p(loss_sum), _p(dh), int(dh_stride), _p(dw), _p(workspace),
+                              ws_bytes, _stream(stream)), "bdvocab_loss")
 
 
 def bdvocab_profile_enable(enable=True):
@@ -119,9 +119,10 @@ class VocabLoss:
         self.row_list = row_list
 
     def __call__(self, h, w_head, targets, weights=None, rows=None, dh=None, lse=None, loss=None, loss_sum=None,
-                 stream=None):
+                 dw=None, stream=None):
         """Fills ``loss`` (allocated when None), ``lse``, ``loss_sum`` and
-        ``dh`` (rows written in place) and returns (loss, lse, loss_sum, dh)."""
+        ``dh`` (rows written in place), adds the head gradient to ``dw``
+        (fp32 [V, d]) when given, and returns (loss, lse, loss_sum, dh)."""
         import torch
         R = self.prob.n_rows
         if (rows is not None) != self.row_list:
@@ -129,5 +130,5 @@ class VocabLoss:
         if loss is None:
             loss = torch.empty(R, dtype=torch.float32, device=h.device)
         bdvocab_loss(self.prob, h, h.stride(0), w_head, rows, targets, weights, lse, loss, loss_sum, dh,
-                     0 if dh is None else dh.stride(0), self.workspace, stream)
+                     0 if dh is None else dh.stride(0), dw, self.workspace, stream)
         return loss, lse, loss_sum, dh

@@ -11,6 +11,7 @@
 //   rows          lse, loss, G = w (softmax - onehot) in bf16 over S
 //   grad GEMM     dH_chunk[n, d] = G W              (bf16 or fp32)
 //   (scatter)     packed dh rows -> their positions
+//   head GEMM     dW[V, d] += G^T H_chunk           (fp32, when requested)
 // In the GEMM library's column-major terms a row-major [r, c] matrix with
 // pitch p is a c x r matrix with leading dimension p, so the logits GEMM is
 // S^T (V x n) = op_T(W^T as d x V) * (H^T as d x n) and the gradient GEMM
@@ -22,7 +23,9 @@
 // Algorithm choice: on the first use of a shape, the library's top
 // candidates are timed on the call's stream (which synchronises that first
 // call) and the fastest is kept for the process; BDVOCAB_TUNE=0 in the
-// environment keeps the library's first candidate instead.
+// environment keeps the library's first candidate instead.  The head GEMM
+// accumulates into the caller's dW, so it is never timed: it takes the
+// library's first candidate.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -91,9 +94,9 @@ Layout layout(const bdvocab_problem& p, bool row_list) {
 }
 
 // ------------------------------------------------------------------ profiling
-enum Kind { K_LOGITS, K_ROWS, K_GRAD, K_GATHER, K_SCATTER, K_SUM, K_TRANSPOSE, K_COUNT };
+enum Kind { K_LOGITS, K_ROWS, K_GRAD, K_GATHER, K_SCATTER, K_SUM, K_TRANSPOSE, K_HEAD, K_COUNT };
 const char* kKindNames[K_COUNT] = {"logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum",
-                                   "transpose"};
+                                   "transpose", "head_grad_gemm"};
 
 struct Prof {
   std::mutex mu;
@@ -138,10 +141,10 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? BDVOCAB_OK : BDVOCAB_EHIP; }
 struct GemmKey {
   int dev, ta, tb;
   int64_t m, n, k, lda, ldb, ldd;
-  int dtype;
+  int dtype, accumulate;
   bool operator<(const GemmKey& o) const {
-    return std::tie(dev, ta, tb, m, n, k, lda, ldb, ldd, dtype) <
-           std::tie(o.dev, o.ta, o.tb, o.m, o.n, o.k, o.lda, o.ldb, o.ldd, o.dtype);
+    return std::tie(dev, ta, tb, m, n, k, lda, ldb, ldd, dtype, accumulate) <
+           std::tie(o.dev, o.ta, o.tb, o.m, o.n, o.k, o.lda, o.ldb, o.ldd, o.dtype, o.accumulate);
   }
 };
 
@@ -162,10 +165,10 @@ struct GemmDescs {
   }
 };
 
-// D (m x n, column-major, leading dimension ldd, type dt) = op(A) op(B),
-// A and B bf16; alpha = 1, beta = 0.
+// D (m x n, column-major, leading dimension ldd, type dt) = op(A) op(B)
+// (+ D when accumulate), A and B bf16.
 int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, const void* B,
-         int64_t ldb, void* D, hipDataType dt, int64_t ldd, void* ws, hipStream_t s) {
+         int64_t ldb, void* D, hipDataType dt, int64_t ldd, void* ws, hipStream_t s, bool accumulate = false) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BDVOCAB_EHIP;
   hipblasLtHandle_t h;
@@ -191,7 +194,7 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
       hipblasLtMatrixLayoutCreate(&g.b, HIP_R_16BF, tb ? n : k, tb ? k : n, ldb) != HIPBLAS_STATUS_SUCCESS ||
       hipblasLtMatrixLayoutCreate(&g.d, dt, m, n, ldd) != HIPBLAS_STATUS_SUCCESS)
     return BDVOCAB_EBLAS;
-  const GemmKey key{dev, ta, tb, m, n, k, lda, ldb, ldd, (int)dt};
+  const GemmKey key{dev, ta, tb, m, n, k, lda, ldb, ldd, (int)dt, accumulate ? 1 : 0};
   hipblasLtMatmulHeuristicResult_t best{};
   {
     std::lock_guard<std::mutex> lk(g_blas.mu);
@@ -211,7 +214,7 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
       if (st != HIPBLAS_STATUS_SUCCESS || found < 1) return BDVOCAB_EBLAS;
       int pick = -1;
       const char* env = std::getenv("BDVOCAB_TUNE");
-      const bool tune = found > 1 && !(env && std::strcmp(env, "0") == 0);
+      const bool tune = found > 1 && !accumulate && !(env && std::strcmp(env, "0") == 0);
       if (tune) {
         hipEvent_t e0 = nullptr, e1 = nullptr;
         if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return BDVOCAB_EHIP;
@@ -246,8 +249,8 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
     }
   }
   const float one = 1.f, zero = 0.f;
-  const hipblasStatus_t st = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, &zero, D, g.d, D, g.d, &best.algo, ws,
-                                             kBlasWs, s);
+  const hipblasStatus_t st = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, accumulate ? &one : &zero, D, g.d, D,
+                                             g.d, &best.algo, ws, kBlasWs, s);
   return st == HIPBLAS_STATUS_SUCCESS ? BDVOCAB_OK : BDVOCAB_EBLAS;
 }
 
@@ -265,7 +268,7 @@ size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list) {
 
 int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride, const void* w_head,
                  const int32_t* rows, const int32_t* targets, const float* weights, float* lse, float* loss,
-                 float* loss_sum, void* dh, int64_t dh_stride, void* workspace, size_t ws_bytes,
+                 float* loss_sum, void* dh, int64_t dh_stride, float* dw, void* workspace, size_t ws_bytes,
                  void* hip_stream) {
   const int pc = check_problem(problem);
   if (pc != BDVOCAB_OK) return pc;
@@ -278,6 +281,7 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
     if (!h || !w_head || !targets || !loss) return BDVOCAB_EINVAL;
     if (h_stride < d || h_stride % 8 != 0 || !aligned16(h) || !aligned16(w_head)) return BDVOCAB_EINVAL;
     if (dh && (dh_stride < d || (dh_stride * es) % 16 != 0 || !aligned16(dh))) return BDVOCAB_EINVAL;
+    if (dw && !aligned16(dw)) return BDVOCAB_EINVAL;
     const Layout L = layout(p, rows != nullptr);
     if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0 || ws_bytes < L.total)
       return BDVOCAB_EWORKSPACE;
@@ -312,14 +316,24 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
                         lse ? lse + c0 : nullptr, loss + c0};
       rc = timed(K_ROWS, s, [&] { return hip_rc(launch_rows(ra, s)); });
       if (rc != BDVOCAB_OK) return rc;
-      if (!dh) continue;
-      void* D = rows ? static_cast<void*>(dhc) : static_cast<void*>(static_cast<uint8_t*>(dh) + c0 * dh_stride * es);
-      const int64_t ldd = rows ? d : dh_stride;
-      rc = timed(K_GRAD, s, [&] { return gemm(true, false, d, n, p.vocab, wt, L.ld, S, 2 * L.ld, D, dt, ldd, blas_ws, s); });
-      if (rc != BDVOCAB_OK) return rc;
-      if (rows) {
-        const ScatterArgs sa{dhc, n, (int32_t)d, es, rows + c0, static_cast<uint8_t*>(dh), dh_stride};
-        rc = timed(K_SCATTER, s, [&] { return hip_rc(launch_scatter(sa, s)); });
+      if (dh) {
+        void* D = rows ? static_cast<void*>(dhc)
+                       : static_cast<void*>(static_cast<uint8_t*>(dh) + c0 * dh_stride * es);
+        const int64_t ldd = rows ? d : dh_stride;
+        rc = timed(K_GRAD, s,
+                   [&] { return gemm(true, false, d, n, p.vocab, wt, L.ld, S, 2 * L.ld, D, dt, ldd, blas_ws, s); });
+        if (rc != BDVOCAB_OK) return rc;
+        if (rows) {
+          const ScatterArgs sa{dhc, n, (int32_t)d, es, rows + c0, static_cast<uint8_t*>(dh), dh_stride};
+          rc = timed(K_SCATTER, s, [&] { return hip_rc(launch_scatter(sa, s)); });
+          if (rc != BDVOCAB_OK) return rc;
+        }
+      }
+      if (dw) {
+        // dW^T (d x V) += (H^T as d x n) * op_T(G^T as V x n)
+        rc = timed(K_HEAD, s, [&] {
+          return gemm(false, true, d, p.vocab, n, Hb, ldh, S, 2 * L.ld, dw, HIP_R_32F, d, blas_ws, s, true);
+        });
         if (rc != BDVOCAB_OK) return rc;
       }
     }

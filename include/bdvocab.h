@@ -17,15 +17,20 @@
  *   s_r    = h_r W^T                         (the row's V logits)
  *   lse_r  = log sum_v exp(s_rv)
  *   loss_r = w_r (lse_r - s_r[y_r])
- *   dh_r   = w_r (softmax(s_r) - e_{y_r}) W   (gradient of loss_r wrt h_r)
- * The head is frozen: no gradient for W is formed.  A row whose target is
- * outside [0, V) is ignored: loss_r = 0, dh_r = 0 (lse_r is still written).
+ *   g_r    = w_r (softmax(s_r) - e_{y_r})     (gradient of loss_r wrt s_r)
+ *   dh_r   = g_r W                            (gradient of loss_r wrt h_r)
+ *   dW     = sum_r g_r^T h_r                  (gradient of the summed loss wrt W)
+ * dW is optional: the speculative-decoding row streams through a frozen
+ * head (no dW), the block-diffusion row does not say the head is frozen.
+ * A row whose target is outside [0, V) is ignored: loss_r = 0, dh_r = 0,
+ * no dW term (lse_r is still written).
  *
  * How.  Rows go in chunks of C.  Per chunk: the chunk's logits in fp32
  * (a plain library GEMM, bf16 inputs, fp32 accumulation) into the
  * workspace; one fused pass per row forms lse, the loss and the logit
  * gradient, written in bf16 over the same workspace rows; a second library
- * GEMM forms dh from a transposed copy of the head made once per call.
+ * GEMM forms dh from a transposed copy of the head made once per call, and
+ * a third, when dW is requested, adds the chunk's G^T H to dW.
  * Device memory for logits is C * V * 4 bytes, never R * V.  The first call
  * of a shape times the GEMM library's candidate algorithms on the call's
  * stream (synchronising that call) and keeps the fastest; BDVOCAB_TUNE=0
@@ -95,13 +100,18 @@ size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list);
  *            Row idx_r of dh (at dh + idx_r * dh_stride elements) is
  *            written for every r; other rows are not touched.  dh_stride
  *            >= d.
+ *   dw       fp32 [V, d] row-major, contiguous, device, or NULL.  The call
+ *            ADDS its gradient (dw += sum_r g_r^T h_r), so the caller
+ *            clears it before the first call of a step.  Its GEMM takes the
+ *            library's first algorithm (never the timing search, whose runs
+ *            would accumulate).
  *   workspace / ws_bytes: at least bdvocab_workspace_bytes(problem,
  *            rows != NULL); the contents need not be initialised.
  * R = 0 enqueues only the zeroing of loss_sum. */
 int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride,
                  const void* w_head, const int32_t* rows, const int32_t* targets,
                  const float* weights, float* lse, float* loss, float* loss_sum,
-                 void* dh, int64_t dh_stride, void* workspace, size_t ws_bytes,
+                 void* dh, int64_t dh_stride, float* dw, void* workspace, size_t ws_bytes,
                  void* hip_stream);
 
 /* Static text for a bdvocab_status value. */
@@ -110,7 +120,7 @@ const char* bdvocab_status_string(int status);
 /* Kernel timing for measurement: when enabled (nonzero), every launch of
  * bdvocab_loss is bracketed by HIP events on its stream, per kind:
  * "logits_gemm", "rows", "grad_gemm", "gather", "scatter", "loss_sum",
- * "transpose".
+ * "transpose", "head_grad_gemm".
  * bdvocab_profile_read synchronises the recorded events, writes up to `cap`
  * (name, launch count, total milliseconds) entries for the kinds that ran,
  * sets *n to their number and clears the record. */

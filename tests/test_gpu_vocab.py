@@ -6,7 +6,9 @@ the logit gradient is rounded to bf16 before the gradient GEMM, a relative
 error of at most 2^-9 per term):
   lse and per-row loss: max |err| <= 1e-3 (the LSE bar of the attention path);
   loss sum: relative error <= 1e-4;
-  dh: relative L2 error <= 1e-2 on every row (the gradient bar).
+  dh: relative L2 error <= 1e-2 on every row (the gradient bar);
+  dW (head gradient, fp32 accumulation of bf16 products): relative L2
+  error <= 1e-2 over the whole [V, d] matrix.
 Rows outside the row list keep their contents; ignored targets give loss 0
 and dh 0.
 """
@@ -36,7 +38,8 @@ def _host(t):
     return t.detach().float().cpu().numpy()
 
 
-def _run(dev, seed, T, R, V, d, chunk, row_list, dh_dtype, weighted=True, ignored=(), head_std=None):
+def _run(dev, seed, T, R, V, d, chunk, row_list, dh_dtype, weighted=True, ignored=(), head_std=None, head_grad=True,
+         dw_repeat=1, with_dh=True):
     from block_diffusion_lm_bdlm_amd import bdvocab as BV
     from block_diffusion_lm_bdlm_amd import synth
     print(f"\n[vocab] seed={seed} T={T} R={R} V={V} d={d} chunk={chunk} rows={row_list} dh={dh_dtype}", flush=True)
@@ -57,12 +60,20 @@ def _run(dev, seed, T, R, V, d, chunk, row_list, dh_dtype, weighted=True, ignore
     lse = torch.empty(R, dtype=torch.float32, device=dev)
     loss_sum = torch.empty(1, dtype=torch.float32, device=dev)
     rows_dev = None if rows is None else rows.to(dev)
-    loss, _, _, _ = vl(h, W, y, weights=wt, rows=rows_dev, dh=dh, lse=lse, loss_sum=loss_sum)
+    dw = torch.zeros((V, d), dtype=torch.float32, device=dev) if head_grad else None
+    for _ in range(dw_repeat):
+        loss, _, _, _ = vl(h, W, y, weights=wt, rows=rows_dev, dh=dh if with_dh else None, lse=lse,
+                           loss_sum=loss_sum, dw=dw)
     torch.cuda.synchronize()
     idx = np.arange(R) if rows is None else rows.numpy()
-    lse_ref, loss_ref, dh_ref = ov.vocab_loss_rows(_host(h), _host(W), idx, y.cpu().numpy(), wt.cpu().numpy())
-    return dict(lse=_host(lse), loss=_host(loss), sum=float(loss_sum.item()), dh=_host(dh), idx=idx,
-                lse_ref=lse_ref, loss_ref=loss_ref, dh_ref=dh_ref, T=T)
+    hh, Wh, yh, wh = _host(h), _host(W), y.cpu().numpy(), wt.cpu().numpy()
+    lse_ref, loss_ref, dh_ref = ov.vocab_loss_rows(hh, Wh, idx, yh, wh)
+    out = dict(lse=_host(lse), loss=_host(loss), sum=float(loss_sum.item()), dh=_host(dh), idx=idx,
+               lse_ref=lse_ref, loss_ref=loss_ref, dh_ref=dh_ref, T=T, with_dh=with_dh)
+    if head_grad:
+        out["dw"] = _host(dw)
+        out["dw_ref"] = dw_repeat * ov.vocab_head_grad(hh[idx], Wh, yh, wh)
+    return out
 
 
 def _check(res):
@@ -70,6 +81,11 @@ def _check(res):
     assert max_abs(res["loss"], res["loss_ref"]) <= TOL_LSE
     ref_sum = float(res["loss_ref"].sum())
     assert abs(res["sum"] - ref_sum) <= TOL_SUM * max(1.0, abs(ref_sum))
+    if "dw" in res:
+        assert rel_l2(res["dw"], res["dw_ref"]) <= TOL_GRAD
+    if not res["with_dh"]:
+        assert np.all(res["dh"] == SENTINEL)
+        return
     dh = res["dh"][res["idx"]]
     for r in range(len(res["idx"])):
         if np.any(res["dh_ref"][r]):
@@ -117,10 +133,22 @@ def test_vocab_large_logits(dev):
     _check(_run(dev, 12, 128, 128, 20000, 256, 0, False, 0, head_std=30.0 / 16.0))
 
 
+def test_vocab_head_grad_accumulates_and_alone(dev):
+    # two calls add twice the gradient; a call with dW but no dh leaves dh alone
+    _check(_run(dev, 14, 300, 150, 2500, 64, 64, True, 0, dw_repeat=2))
+    _check(_run(dev, 15, 90, 90, 3001, 128, 32, False, 1, with_dh=False))
+
+
+def test_vocab_head_grad_full_vocabulary(dev):
+    # the benchmark's vocabulary (131,072) with a narrower hidden size so the
+    # fp64 oracle of the whole [V, d] gradient stays small; ragged chunks
+    _check(_run(dev, 16, 500, 96, 131072, 1024, 40, True, 0))
+
+
 def test_vocab_zero_rows(dev):
     from block_diffusion_lm_bdlm_amd import bdvocab as BV
     s = torch.full((1,), 5.0, device=dev)
-    BV.bdvocab_loss(BV.problem(0, 100, 64), None, 64, None, None, None, None, None, None, s, None, 0, None)
+    BV.bdvocab_loss(BV.problem(0, 100, 64), None, 64, None, None, None, None, None, None, s, None, 0, None, None)
     torch.cuda.synchronize()
     assert s.item() == 0.0
 

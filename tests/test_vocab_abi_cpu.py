@@ -72,27 +72,27 @@ class _Fake:
 def test_invalid_arguments_rejected_on_host():
     for bad in [BV.problem(-1, 10, 8), BV.problem(1, 0, 8), BV.problem(1, 10, 0), BV.problem(1, 10, 8, -1)]:
         assert BV.bdvocab_workspace_bytes(bad, False) == 0
-        assert _status(bad, None, 8, None, None, None, None, None, None, None, None, 0, None) == BV.BDVOCAB_EINVAL
+        assert _status(bad, None, 8, None, None, None, None, None, None, None, None, 0, None, None) == BV.BDVOCAB_EINVAL
     for bad in [BV.problem(4, 10, 12), BV.problem(4, 10, 4), BV.problem(4, 10, 8, 0, 2)]:
         assert BV.bdvocab_workspace_bytes(bad, False) == 0
-        assert _status(bad, None, 8, None, None, None, None, None, None, None, None, 0, None) == BV.BDVOCAB_ENOTSUP
+        assert _status(bad, None, 8, None, None, None, None, None, None, None, None, 0, None, None) == BV.BDVOCAB_ENOTSUP
     p = BV.problem(4, 100, 64)
     ws_need = BV.bdvocab_workspace_bytes(p, False)
     h, w, y, loss, ws = _Fake(4096), _Fake(8192), _Fake(12288), _Fake(16384), _Fake(1 << 20, ws_need)
-    assert _status(p, None, 64, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL   # no h
-    assert _status(p, h, 64, w, None, None, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL  # no targets
-    assert _status(p, h, 64, w, None, y, None, None, None, None, None, 0, ws) == BV.BDVOCAB_EINVAL     # no loss
-    assert _status(p, h, 32, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL     # stride < d
-    assert _status(p, h, 68, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL     # stride % 8
-    assert _status(p, _Fake(4098), 64, w, None, y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EINVAL
-    assert _status(p, h, 64, w, None, y, None, None, loss, None, _Fake(20480), 60, ws) == BV.BDVOCAB_EINVAL
+    assert _status(p, None, 64, w, None, y, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EINVAL   # no h
+    assert _status(p, h, 64, w, None, None, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EINVAL  # no targets
+    assert _status(p, h, 64, w, None, y, None, None, None, None, None, 0, None, ws) == BV.BDVOCAB_EINVAL     # no loss
+    assert _status(p, h, 32, w, None, y, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EINVAL     # stride < d
+    assert _status(p, h, 68, w, None, y, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EINVAL     # stride % 8
+    assert _status(p, _Fake(4098), 64, w, None, y, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EINVAL
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, _Fake(20480), 60, None, ws) == BV.BDVOCAB_EINVAL
     small = _Fake(1 << 20, ws_need - 1)
-    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, small) == BV.BDVOCAB_EWORKSPACE
-    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, _Fake((1 << 20) + 16, ws_need)) \
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, None, small) == BV.BDVOCAB_EWORKSPACE
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, None, _Fake((1 << 20) + 16, ws_need)) \
         == BV.BDVOCAB_EWORKSPACE
     # a row list needs the larger workspace
-    assert _status(p, h, 64, w, _Fake(24576), y, None, None, loss, None, None, 0, ws) == BV.BDVOCAB_EWORKSPACE
+    assert _status(p, h, 64, w, _Fake(24576), y, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EWORKSPACE
     # no rows and no loss sum: nothing to do, no HIP call
-    assert _status(BV.problem(0, 100, 64), None, 64, None, None, None, None, None, None, None, None, 0, None) \
+    assert _status(BV.problem(0, 100, 64), None, 64, None, None, None, None, None, None, None, None, 0, None, None) \
         == BV.BDVOCAB_OK
     assert BV.bdvocab_status_string(BV.BDVOCAB_EBLAS).startswith("GEMM library")
