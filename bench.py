@@ -93,6 +93,48 @@ def visible_pairs(L, M, window=0, token_causal=False):
     return int(clean.sum() + corr.sum())
 
 
+def tile_counts(L, M, qt=128, kt=64):
+    """(visited, total) (query tile, key tile) pairs per head of the whole
+    block-causal mask at the forward kernel's granularity (128 query rows,
+    64 keys), from the mask geometry: a clean query tile sees the clean
+    keys up to the end of its last row's block; a corrupted query tile sees
+    the clean keys before its last row's block and the corrupted keys of
+    its own blocks.  Key tiles of the clean and corrupted key spaces start
+    at 0 and at L."""
+    a = np.arange(0, L, qt, dtype=np.int64)
+    last = np.minimum(a + qt, L) - 1
+    clean_end = (last // M + 1) * M
+    visited = ((clean_end + kt - 1) // kt).sum()
+    corr_clean = (last // M) * M
+    own_lo, own_hi = (a // M) * M, (last // M + 1) * M
+    visited += ((corr_clean + kt - 1) // kt).sum() + ((own_hi + kt - 1) // kt - own_lo // kt).sum()
+    nkt = 2 * ((L + kt - 1) // kt)
+    return int(visited), int(2 * len(a) * nkt)
+
+
+def gpu_clock_sample(delay_s, out):
+    """Sample the GPU's current clock with rocm-smi after `delay_s` (run in a
+    thread while the timed steps execute); stores the sclk lines or None."""
+    import subprocess
+    time.sleep(delay_s)
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()]
+        out.append("; ".join(lines) if lines else None)
+    except Exception:  # measurement aid only
+        out.append(None)
+
+
+def frac_at_clock(tflops, clock_line):
+    """Useful TFLOP/s over the bf16 peak scaled from 2.4 GHz to the sampled
+    clock (the first "(NNNNMhz)" in the rocm-smi line), or None."""
+    import re
+    m = re.search(r"\((\d+)\s*Mhz\)", clock_line or "", re.I)
+    if not m:
+        return None
+    return round(tflops / (PEAK_BF16_TFLOPS * int(m.group(1)) / 2400.0), 4)
+
+
 def kernel_flops(name, pairs, hq, batch, d):
     """Algorithmic FLOPs one launch of each kernel performs on visible pairs:
     forward 4d (QK^T, PV); dK/dV kernel 8d (QK^T, dO V^T, P^T dO, dS^T Q);
@@ -456,11 +498,13 @@ def main():
     lse = torch.empty(batch, n2, hq, dtype=torch.float32, device=dev)
     L_ = L
 
-    def step():
+    def step(mid=None):
         for g_ in grads[:5]:
             g_.zero_()
         B.bdattn_fwd(wm.prob, wm.share, wm.kv, q[:, :L_], q[:, L_:], k[:, :L_], v[:, :L_], k[:, L_:],
                      v[:, L_:], o, B.BDATTN_BF16, lse, ws_f)
+        if mid is not None:
+            mid.record()
         dq, dkc, dvc, dkx, dvx, delta = grads
         B.bdattn_bwd(wm.prob, wm.share, wm.kv, q[:, :L_], q[:, L_:], k[:, :L_], v[:, :L_], k[:, L_:],
                      v[:, L_:], o, B.BDATTN_BF16, lse, do, delta, 0, dq, dkc, dvc, dkx, dvx, ws_b)
@@ -469,23 +513,38 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    B.bdattn_plan_order(wm.prob, wm.share, wm.kv)  # the host plan of the whole-mask call
+    plan_ms = (time.perf_counter() - t0) * 1e3
     B.bdattn_profile_read()  # drop anything recorded so far
     B.bdattn_profile_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    clock = []
+    import threading
+    clk = threading.Thread(target=gpu_clock_sample, args=(0.25, clock), daemon=True)
     torch.cuda.synchronize()
+    clk.start()
     e0.record()
     for i in range(args.steps):
-        step()
+        marks[i][0].record()
+        step(marks[i][1])
+        marks[i][2].record()
     e1.record()
     torch.cuda.synchronize()
+    clk.join(timeout=30)
     B.bdattn_profile_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
     prof = B.bdattn_profile_read()
+    step_ms = [m[0].elapsed_time(m[2]) for m in marks]
+    fwd_ms = [m[0].elapsed_time(m[1]) for m in marks]
+    bwd_ms = [m[1].elapsed_time(m[2]) for m in marks]
     print(f"[bench] {args.steps} steps, {ms:.2f} ms/step; kernels: "
           + ", ".join(f"{n} {c}x {t / c:.3f} ms" for n, (c, t) in sorted(prof.items(), key=lambda x: -x[1][1])),
           file=sys.stderr, flush=True)
 
     pairs = visible_pairs(L, M)
+    tiles = tile_counts(L, M)
     useful = 14.0 * d * pairs * hq * batch
     tflops = useful / (ms * 1e-3) / 1e12
     # dominant kernel by time
@@ -526,6 +585,17 @@ def main():
         # the stricter count: 12*d per pair (forward 4d, backward 8d without
         # the recomputed Q K^T)
         "useful_tflops_12d": round(12.0 / 14.0 * tflops, 2),
+        # per-step events: forward = accumulator zeroing + forward call, backward = backward call
+        "step_ms": {"median": round(float(np.median(step_ms)), 3), "min": round(min(step_ms), 3),
+                    "max": round(max(step_ms), 3)},
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 3),
+        "bwd_ms_median": round(float(np.median(bwd_ms)), 3),
+        "plan_ms": round(plan_ms, 3),
+        "tiles_per_head": {"visited": tiles[0], "total": tiles[1], "skipped_frac": round(1 - tiles[0] / tiles[1], 4),
+                           "granularity": "128 query rows x 64 keys"},
+        "gpu_clock": clock[0] if clock else None,
+        # the 2.5 PF figure assumes 2.4 GHz; the same peak scaled to the sampled clock
+        "frac_of_peak_at_clock": frac_at_clock(tflops, clock[0] if clock else None),
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,

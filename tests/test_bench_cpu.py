@@ -20,3 +20,23 @@ def test_share_pairs_match_oracle_mask(orc, L, M, blocks, clean):
     rows = [t for lo, hi in clean for t in range(lo, hi)] + [L + b * M + i for b in blocks for i in range(M)]
     n = sum(orc.visible(p, i, j) for i in rows for j in range(2 * L))
     assert bench.share_pairs(L, M, sorted(blocks), clean) == n
+
+
+@pytest.mark.parametrize("L,M", [(256, 32), (384, 16), (512, 64)])
+def test_tile_counts_brute_force(L, M):
+    """Visited (128-row, 64-key) tile pairs of the whole block-causal mask,
+    against a pair-by-pair scan of the mask."""
+    import bench
+
+    def seen(qa, ka):
+        for r in range(qa, min(qa + 128, 2 * L)):
+            for k in range(ka, min(ka + 64, 2 * L)):
+                if r < L:
+                    if k < L and k // M <= r // M:
+                        return True
+                elif (k < L and k // M < (r - L) // M) or (k >= L and (k - L) // M == (r - L) // M):
+                    return True
+        return False
+
+    vis = sum(seen(qa, ka) for qa in range(0, 2 * L, 128) for ka in range(0, 2 * L, 64))
+    assert bench.tile_counts(L, M) == (vis, (2 * L // 128) * (2 * L // 64))
