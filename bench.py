@@ -252,6 +252,7 @@ def report_all(reps=3):
         rows.append((name, ms, flops, batch * L, kern))
         del q, k, v, do, wm, wf, wb, grads, state
         torch.cuda.empty_cache()
+    merge_bytes = {}
     shares = [("csbp_L256K_P8_r0_h32kv8", 3, 262144, 32, 32, 8, 8, False, 0.0),
               ("csbp_L512K_P16_r0_h32kv4_outliers", 4, 524288, 16, 32, 4, 16, True, 0.01)]
     for name, idx, L, M, hq, hkv, P, clean_queries, outl in shares:
@@ -286,6 +287,10 @@ def report_all(reps=3):
 
         ms, kern = timed(step)
         flops = 14 * d * share_pairs(L, M, blocks, clean_q) * hq
+        # merge: per merged row, read two (O, LSE) partials and write one in fp32, plus
+        # the bf16 O of the last merge: P merges of R * hq rows per step
+        mrows = sh.R * hq
+        merge_bytes[name] = P * mrows * 3 * (4 * d + 4) + mrows * 2 * d
         rows.append((name, ms, flops, L // P, kern))
         del qc, qx, kx, vx, kc, vc, sh, do, wf, wb, grads
         torch.cuda.empty_cache()
@@ -297,10 +302,16 @@ def report_all(reps=3):
               file=sys.stderr)
         print("    kernels (ms per step): " + ", ".join(f"{n} {t:.3f}" for n, t in sorted(kern.items(), key=lambda x: -x[1])),
               file=sys.stderr)
-        print(json.dumps({"workload": name, "ms": round(ms, 3), "useful_tflops": round(tf, 2),
-                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "tokens_per_s": round(toks / (ms * 1e-3), 1),
-                          "kernels_ms": {n: round(t, 4) for n, t in kern.items()}}), flush=True)
+        line = {"workload": name, "ms": round(ms, 3), "useful_tflops": round(tf, 2),
+                "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "tokens_per_s": round(toks / (ms * 1e-3), 1),
+                "kernels_ms": {n: round(t, 4) for n, t in kern.items()}}
+        if name in merge_bytes and kern.get("merge"):
+            gbs = merge_bytes[name] / (kern["merge"] * 1e-3) / 1e9
+            line["merge_roofline"] = {"bound": "hbm", "algorithmic_bytes": merge_bytes[name],
+                                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            print(f"    merge: {merge_bytes[name] / 1e9:.2f} GB per step, {gbs:.0f} GB/s", file=sys.stderr)
+        print(json.dumps(line), flush=True)
 
 
 def vocab_cpu_baseline(h, W, rows, y, wt, nrows, seed=0):
