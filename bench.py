@@ -112,24 +112,44 @@ def tile_counts(L, M, qt=128, kt=64):
     return int(visited), int(2 * len(a) * nkt)
 
 
-def gpu_clock_sample(delay_s, out):
-    """Sample the GPU's current clock with rocm-smi after `delay_s` (run in a
-    thread while the timed steps execute); stores the sclk lines or None."""
-    import subprocess
+def _sclk_file():
+    """The pp_dpm_sclk sysfs file of cuda:0's card (matched by PCI address),
+    or None.  Called before the timed region."""
+    import glob
+
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}."
+    except Exception:  # measurement aid only
+        return None
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            if os.path.basename(os.path.realpath(os.path.dirname(f))).lower().startswith(want):
+                return f
+        except OSError:
+            continue
+    return None
+
+
+def gpu_clock_sample(delay_s, path, out):
+    """After `delay_s`, read the current sclk level (the line marked '*') from
+    the card's sysfs file: a plain file read, no process is started.  Runs in
+    a thread while the timed steps execute; stores "(NNNNMhz)" text or None."""
     time.sleep(delay_s)
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        lines = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()]
-        out.append("; ".join(lines) if lines else None)
+        with open(path) as f:
+            cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+        out.append(f"sclk {cur[0]} (pp_dpm_sclk)" if cur else None)
     except Exception:  # measurement aid only
         out.append(None)
 
 
 def frac_at_clock(tflops, clock_line):
     """Useful TFLOP/s over the bf16 peak scaled from 2.4 GHz to the sampled
-    clock (the first "(NNNNMhz)" in the rocm-smi line), or None."""
+    clock (the first "NNNNMhz" in the sysfs line), or None."""
     import re
-    m = re.search(r"\((\d+)\s*Mhz\)", clock_line or "", re.I)
+    m = re.search(r"(\d+)\s*Mhz", clock_line or "", re.I)
     if not m:
         return None
     return round(tflops / (PEAK_BF16_TFLOPS * int(m.group(1)) / 2400.0), 4)
@@ -533,9 +553,11 @@ def main():
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     clock = []
     import threading
-    clk = threading.Thread(target=gpu_clock_sample, args=(0.25, clock), daemon=True)
+    sclk = _sclk_file()
+    clk = threading.Thread(target=gpu_clock_sample, args=(0.25, sclk, clock), daemon=True) if sclk else None
     torch.cuda.synchronize()
-    clk.start()
+    if clk:
+        clk.start()
     e0.record()
     for i in range(args.steps):
         marks[i][0].record()
@@ -543,7 +565,8 @@ def main():
         marks[i][2].record()
     e1.record()
     torch.cuda.synchronize()
-    clk.join(timeout=30)
+    if clk:
+        clk.join(timeout=30)
     B.bdattn_profile_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
     prof = B.bdattn_profile_read()
