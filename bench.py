@@ -449,7 +449,7 @@ def bench_vocab(args):
     cpu = None
     if args.cpu_rows > 0:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        cpu = vocab_cpu_baseline(h, W, rows, y, wt, min(args.cpu_rows, 64))
+        cpu = vocab_cpu_baseline(h, W, rows, y, wt, min(args.cpu_rows, 4096))
     out = {
         "metric": "vocabulary loss rows/s through the frozen head, loss + dh (1 GPU)",
         "value": round(R / (ms * 1e-3), 1),
