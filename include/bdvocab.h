@@ -37,9 +37,10 @@
  * in the environment keeps the library's first candidate.
  *
  * Conventions.
- *   - Device buffers are caller-owned; the library allocates no device
- *     memory (the GEMM library's handle is created once per device).
- *     Scratch comes from `workspace` (size from bdvocab_workspace_bytes).
+ *   - Device buffers are caller-owned and scratch comes from `workspace`
+ *     (size from bdvocab_workspace_bytes).  This library allocates no
+ *     device memory itself; the GEMM library (hipBLASLt) creates its handle
+ *     once per device on the first call and may allocate inside it.
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL =
  *     the null stream); buffers must stay valid until it completes.  Calls
  *     sharing a workspace must not overlap.
