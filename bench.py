@@ -3,8 +3,9 @@
 Default workload (the headline metric's configuration): whole BDLM mask at
 L = 65536 clean tokens (131072 positions), block size M = 32, batch 1,
 40 query heads / 8 KV heads, d_h = 128, bf16 inputs ~ N(0, 1), synthetic.
-One step = zero the gradient accumulators, forward (bf16 O, fp32 LSE),
-backward (dQ, dK, dV) — the whole hot path, nothing skipped.
+One step = forward (bf16 O, fp32 LSE), backward (dQ, dK, dV; the gradient
+kernels write their outputs, so nothing needs zeroing) — the whole hot
+path, nothing skipped.
 
 Useful FLOPs count visible (query, key) pairs only: 4 d per pair forward and
 10 d per pair backward, pairs per head = L (L + M) for the block-causal
@@ -262,9 +263,7 @@ def report_all(reps=3):
         def step():
             fwd()
             if bwd:
-                for g_ in grads[:5]:
-                    g_.zero_()
-                wm.bwd(q, k, v, state["o"], state["lse"], do, ws=wb, grads=grads)
+                wm.bwd(q, k, v, state["o"], state["lse"], do, ws=wb, grads=grads, overwrite=True)
 
         ms, kern = timed(step)
         pairs = visible_pairs(L, M, window) * hq * batch
@@ -530,15 +529,13 @@ def main():
     L_ = L
 
     def step(mid=None):
-        for g_ in grads[:5]:
-            g_.zero_()
         B.bdattn_fwd(wm.prob, wm.share, wm.kv, q[:, :L_], q[:, L_:], k[:, :L_], v[:, :L_], k[:, L_:],
                      v[:, L_:], o, B.BDATTN_BF16, lse, ws_f)
         if mid is not None:
             mid.record()
         dq, dkc, dvc, dkx, dvx, delta = grads
         B.bdattn_bwd(wm.prob, wm.share, wm.kv, q[:, :L_], q[:, L_:], k[:, :L_], v[:, :L_], k[:, L_:],
-                     v[:, L_:], o, B.BDATTN_BF16, lse, do, delta, 0, dq, dkc, dvc, dkx, dvx, ws_b)
+                     v[:, L_:], o, B.BDATTN_BF16, lse, do, delta, B.BDATTN_BWD_OVERWRITE, dq, dkc, dvc, dkx, dvx, ws_b)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -619,7 +616,7 @@ def main():
         # the stricter count: 12*d per pair (forward 4d, backward 8d without
         # the recomputed Q K^T)
         "useful_tflops_12d": round(12.0 / 14.0 * tflops, 2),
-        # per-step events: forward = accumulator zeroing + forward call, backward = backward call
+        # per-step events: forward = forward call, backward = backward call
         "step_ms": {"median": round(float(np.median(step_ms)), 3), "min": round(min(step_ms), 3),
                     "max": round(max(step_ms), 3)},
         "fwd_ms_median": round(float(np.median(fwd_ms)), 3),

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbdattn.s
 BDATTN_OK, BDATTN_EINVAL, BDATTN_ENOTSUP, BDATTN_EHIP, BDATTN_EWORKSPACE = 0, -1, -2, -3, -4
 BDATTN_BF16, BDATTN_F32 = 0, 1
 BDATTN_CLEAN_BLOCK_CAUSAL, BDATTN_CLEAN_TOKEN_CAUSAL = 0, 1
+BDATTN_BWD_DELTA_READY, BDATTN_BWD_OVERWRITE = 1, 2
 BDATTN_MAX_RUNS = 8
 
 
@@ -180,13 +181,15 @@ def bdattn_shard_merge(rows, d, o_acc, lse_acc, o_part, lse_part, o_final_bf16=N
 
 
 def bdattn_bwd(prob, sh, kvs, q_clean, q_corr, k_clean, v_clean, k_corr, v_corr, o_final, o_dtype, lse_final,
-               d_o, delta, delta_ready, dq_acc, dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc,
+               d_o, delta, flags, dq_acc, dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc,
                workspace, stream=None):
+    """flags: BDATTN_BWD_DELTA_READY and/or BDATTN_BWD_OVERWRITE (a bool is
+    read as the delta-ready flag alone)."""
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return _check(lib().bdattn_bwd(C.byref(prob), C.byref(sh), C.byref(kvs), tensor(q_clean), tensor(q_corr),
                                    tensor(k_clean), tensor(v_clean), tensor(k_corr), tensor(v_corr),
                                    tensor(o_final), o_dtype, _p(lse_final), tensor(d_o), _p(delta),
-                                   int(bool(delta_ready)), _p(dq_acc), _p(dk_clean_acc), _p(dv_clean_acc),
+                                   int(flags), _p(dq_acc), _p(dk_clean_acc), _p(dv_clean_acc),
                                    _p(dk_corr_acc), _p(dv_corr_acc), _p(workspace), ws_bytes,
                                    _stream(stream)), "bdattn_bwd")
 

@@ -403,13 +403,23 @@ int bdattn_shard_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, co
 int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const bdattn_kv* kv,
                bdattn_tensor q_clean, bdattn_tensor q_corr, bdattn_tensor k_clean, bdattn_tensor v_clean,
                bdattn_tensor k_corr, bdattn_tensor v_corr, bdattn_tensor o_final, int32_t o_dtype,
-               const float* lse_final, bdattn_tensor d_o, float* delta, int32_t delta_ready, float* dq_acc,
+               const float* lse_final, bdattn_tensor d_o, float* delta, int32_t flags, float* dq_acc,
                float* dk_clean_acc, float* dv_clean_acc, float* dk_corr_acc, float* dv_corr_acc,
                void* workspace, size_t ws_bytes, void* hip_stream) {
   int32_t runs = 0;
   if (!problem_ok(problem) || !share_ok(problem, share, &runs) || !kv_ok(problem, kv)) return BDATTN_EINVAL;
   if (!problem_supported(problem) || problem->dtype != BDATTN_BF16) return BDATTN_ENOTSUP;
   if (o_dtype != BDATTN_BF16 && o_dtype != BDATTN_F32) return BDATTN_EINVAL;
+  if (flags & ~(BDATTN_BWD_DELTA_READY | BDATTN_BWD_OVERWRITE)) return BDATTN_EINVAL;
+  const bool delta_ready = (flags & BDATTN_BWD_DELTA_READY) != 0;
+  const bool overwrite = (flags & BDATTN_BWD_OVERWRITE) != 0;
+  // overwrite is exact only where this one call writes every gradient
+  // element: the whole mask (every row sees its own block, every key is seen
+  // by its own block's rows)
+  if (overwrite && !(share->n_blocks == problem->L / problem->M && share->n_clean == 1 &&
+                     share->clean_lo[0] == 0 && share->clean_hi[0] == problem->L && kv->n == 1 &&
+                     kv->lo[0] == 0 && kv->hi[0] == problem->L && kv->include_local != 0))
+    return BDATTN_EINVAL;
   const Plan P = make_plan(problem, share, kv);
   if (P.R == 0) return BDATTN_OK;
   auto al16 = [](const void* p) { return p && reinterpret_cast<uintptr_t>(p) % 16 == 0; };
@@ -447,10 +457,10 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kh, ws.vh,
-              dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc};
+              dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc, overwrite ? 1 : 0};
   e = timed(K_DKDV, s, [&] { return launch_dkdv(P, ka, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DqArgs qa{ws.qh, ws.doh, ws.lse2, ws.dc, ws.kh, ws.vh, dq_acc};
+  DqArgs qa{ws.qh, ws.doh, ws.lse2, ws.dc, ws.kh, ws.vh, dq_acc, overwrite ? 1 : 0};
   return hip_status(timed(K_DQ, s, [&] { return launch_dq(P, qa, s); }));
 }
 

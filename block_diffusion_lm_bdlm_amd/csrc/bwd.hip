@@ -305,7 +305,7 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
 #pragma unroll
         for (int i = 0; i < 16; i += 4) {
           f32x4* p4 = reinterpret_cast<f32x4*>(dp + db * 32 + crow(i, hh));
-          f32x4 cur = *p4;
+          f32x4 cur = A.overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *p4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) cur[e] += P.scale * dqacc[rb][db][i + e];
           *p4 = cur;

@@ -410,7 +410,7 @@ __device__ __forceinline__ void dkdv_role(const Plan& P, const DkdvArgs& A, Dkdv
 #pragma unroll
       for (int i = 0; i < 16; i += 4) {
         f32x4* pd = reinterpret_cast<f32x4*>(dst + rowoff + db * 32 + crow(i, hh));
-        f32x4 cur4 = *pd;
+        f32x4 cur4 = A.overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *pd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) cur4[e] += f * acc[db][kb][i + e];
         *pd = cur4;

@@ -68,7 +68,8 @@ struct DqArgs {
   const float* dc;
   const _Float16* kh;  // compact key side, fp16 natural
   const _Float16* vh;
-  float* dq;  // [batch][R][hq][d], +=
+  float* dq;  // [batch][R][hq][d], += (= when overwrite)
+  int32_t overwrite;
 };
 
 struct DkdvArgs {
@@ -79,10 +80,11 @@ struct DkdvArgs {
   const int32_t* vis;
   const _Float16* kh;
   const _Float16* vh;
-  float* dk_clean;  // [batch][L][hkv][d], +=
+  float* dk_clean;  // [batch][L][hkv][d], += (= when overwrite)
   float* dv_clean;
-  float* dk_corr;   // [batch][n_corr_rows][hkv][d], +=
+  float* dk_corr;   // [batch][n_corr_rows][hkv][d], += (= when overwrite)
   float* dv_corr;
+  int32_t overwrite;
 };
 
 struct MergeArgs {

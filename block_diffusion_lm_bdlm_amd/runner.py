@@ -63,16 +63,19 @@ class WholeMask:
                      o, dtype_code(o), lse, ws, stream)
         return o, lse
 
-    def bwd(self, q, k, v, o, lse, do, ws=None, stream=None, grads=None):
-        """-> dq [batch, 2L, hq, d] fp32, dk, dv [batch, 2L, hkv, d] fp32."""
+    def bwd(self, q, k, v, o, lse, do, ws=None, stream=None, grads=None, overwrite=False):
+        """-> dq [batch, 2L, hq, d] fp32, dk, dv [batch, 2L, hkv, d] fp32.
+        overwrite: the kernels write the gradients instead of adding to
+        them (``grads`` then need no zeroing)."""
         L, dev = self.L, q.device
         if grads is None:
             grads = self.alloc_grads(dev)
         dq, dkc, dvc, dkx, dvx, delta = grads
         if ws is None:
             ws = self.workspace(True, dev)
+        flags = B.BDATTN_BWD_OVERWRITE if overwrite else 0
         B.bdattn_bwd(self.prob, self.share, self.kv, q[:, :L], q[:, L:], k[:, :L], v[:, :L], k[:, L:], v[:, L:],
-                     o, dtype_code(o), lse, do, delta, 0, dq, dkc, dvc, dkx, dvx, ws, stream)
+                     o, dtype_code(o), lse, do, delta, flags, dq, dkc, dvc, dkx, dvx, ws, stream)
         return dq, torch.cat([dkc, dkx], 1), torch.cat([dvc, dvx], 1)
 
     def alloc_grads(self, dev):

@@ -209,23 +209,31 @@ int bdattn_shard_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
  * per-call contributions of a sharded key set sum to the full gradient.
  *   q_*, k_*, v_*: as in bdattn_fwd (bf16 only).
  *   o_final: share rows x hq, o_dtype BDATTN_BF16 or BDATTN_F32; read only
- *          when delta_ready == 0 (to form D), otherwise not validated.
+ *          when D is formed here (flags without BDATTN_BWD_DELTA_READY),
+ *          otherwise not validated.
  *   lse_final: fp32 [batch][R][hq].   d_o: share rows x hq, bf16.
- *   delta: fp32 [batch][R][hq], D = rowsum(dO * O).  delta_ready == 0:
- *          computed here and stored; != 0: read as given (reuse across the
- *          calls of one step).
+ *   delta: fp32 [batch][R][hq], D = rowsum(dO * O).  Without
+ *          BDATTN_BWD_DELTA_READY: computed here and stored; with it: read
+ *          as given (reuse across the calls of one step).
+ *   flags: BDATTN_BWD_DELTA_READY (1) as above; BDATTN_BWD_OVERWRITE (2):
+ *          the gradients are written, not added, so they need no zeroing.
+ *          Only for the whole-mask form (every block, clean query range
+ *          [0, L), key range [0, L) and include_local), where this one call
+ *          produces every element; any other call with it is BDATTN_EINVAL.
  *   dq_acc: fp32 [batch][R][hq][d] contiguous, += this call's part.
  *   dk_clean_acc, dv_clean_acc: fp32 [batch][L][hkv][d] contiguous (token
  *          rows), += (may be NULL when the call has no clean key range).
  *   dk_corr_acc, dv_corr_acc: fp32 [batch][n_blocks*M][hkv][d] contiguous
  *          (packed corrupted rows), += (may be NULL when include_local == 0).
- * Accumulators must be zeroed by the caller before the first call. */
+ * Without BDATTN_BWD_OVERWRITE the accumulators must be zeroed by the caller
+ * before the first call. */
+enum { BDATTN_BWD_DELTA_READY = 1, BDATTN_BWD_OVERWRITE = 2 };
 int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share,
                const bdattn_kv* kv, bdattn_tensor q_clean, bdattn_tensor q_corr,
                bdattn_tensor k_clean, bdattn_tensor v_clean,
                bdattn_tensor k_corr, bdattn_tensor v_corr,
                bdattn_tensor o_final, int32_t o_dtype, const float* lse_final,
-               bdattn_tensor d_o, float* delta, int32_t delta_ready,
+               bdattn_tensor d_o, float* delta, int32_t flags,
                float* dq_acc, float* dk_clean_acc, float* dv_clean_acc,
                float* dk_corr_acc, float* dv_corr_acc, void* workspace,
                size_t ws_bytes, void* hip_stream);

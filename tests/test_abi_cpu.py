@@ -152,3 +152,27 @@ def test_invalid_arguments_rejected_on_host():
     assert _status(B.bdattn_shard_merge, 0, 128, None, None, None, None, None, 0) == B.BDATTN_OK
     assert _status(B.bdattn_assign_blocks, 10, 3, 0) == B.BDATTN_EINVAL
     assert B.bdattn_status_string(-4).startswith("workspace")
+
+
+def test_bwd_flags_rejected_on_host():
+    """Overwrite is accepted only for the whole-mask call; unknown flag bits
+    are rejected.  Both before any HIP call."""
+    p = B.problem(1, 1024, 16, 4, 2, 128)
+    whole_s, whole_k = B.share(range(64), [(0, 1024)]), B.kv([(0, 1024)], True)
+    part_s = B.share(range(32), [(0, 512)])
+    shard_k = B.kv([(0, 512)], False)
+    none = [None] * 7
+
+    def st(sh, kv, flags):
+        try:
+            B.bdattn_bwd(p, sh, kv, *none, B.BDATTN_BF16, None, None, None, flags, None, None, None, None, None,
+                         None, stream=0)
+        except B.BdattnError as e:
+            return e.status
+        return B.BDATTN_OK
+
+    assert st(part_s, whole_k, B.BDATTN_BWD_OVERWRITE) == B.BDATTN_EINVAL
+    assert st(whole_s, shard_k, B.BDATTN_BWD_OVERWRITE) == B.BDATTN_EINVAL
+    assert st(whole_s, whole_k, 4) == B.BDATTN_EINVAL
+    # the whole-mask call passes the flag check and fails later on its missing tensors
+    assert st(whole_s, whole_k, B.BDATTN_BWD_OVERWRITE | B.BDATTN_BWD_DELTA_READY) == B.BDATTN_EINVAL

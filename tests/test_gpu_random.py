@@ -118,3 +118,31 @@ def test_random_csbp_share(dev, orc, i):
     assert rel_l2(dvc[0].cpu().numpy(), dv_ref[0, :L]) <= TOL_GRAD
     assert rel_l2(dkx[0].cpu().numpy(), dk_ref[0, kx]) <= TOL_GRAD
     assert rel_l2(dvx[0].cpu().numpy(), dv_ref[0, kx]) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_whole_mask_overwrite(dev, orc, i):
+    """The whole-mask backward with BDATTN_BWD_OVERWRITE on gradients
+    pre-filled with NaN: every element must be written (an element left
+    alone stays NaN and fails), and the values must match the oracle."""
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd.runner import WholeMask
+    batch, L, M, hq, hkv, d, tc, W = _case(i)
+    print(f"\n[overwrite case {i}] batch={batch} L={L} M={M} hq={hq} hkv={hkv} d={d} token_causal={tc} window={W}",
+          flush=True)
+    q, k, v, do = doubled_inputs(8000 + i, batch, L, hq, hkv, d, device=dev)
+    wm = WholeMask(batch, L, M, hq, hkv, d, B.BDATTN_BF16,
+                   B.BDATTN_CLEAN_TOKEN_CAUSAL if tc else B.BDATTN_CLEAN_BLOCK_CAUSAL, window=W)
+    o, lse = wm.fwd(q, k, v, o_dtype=torch.float32)
+    grads = wm.alloc_grads(dev)
+    for g_ in grads[:5]:
+        g_.fill_(float("nan"))
+    dq, dk, dv = wm.bwd(q, k, v, o, lse, do, grads=grads, overwrite=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dq).any() and not torch.isnan(dk).any() and not torch.isnan(dv).any()
+    p = orc.problem(batch, L, M, hq, hkv, d, token_causal=tc, bf16=True, window=W)
+    hq_, hk_, hv_, hdo = (host_bits(x) for x in (q, k, v, do))
+    dq_ref, dk_ref, dv_ref = orc.bwd(p, orc.share(), orc.keys(), orc.keys(), hq_, hk_, hv_, hdo)
+    assert rel_l2(dq.cpu().numpy(), dq_ref) <= TOL_GRAD
+    assert rel_l2(dk.cpu().numpy(), dk_ref) <= TOL_GRAD
+    assert rel_l2(dv.cpu().numpy(), dv_ref) <= TOL_GRAD
