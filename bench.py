@@ -421,10 +421,13 @@ def bench_vocab(args):
                  "avg_ms": round(rms / rc, 3)}
     # the same step with the head trained: dW cleared, then accumulated per chunk
     dw = torch.zeros((V, d), dtype=torch.float32, device=dev)
+    del vl
+    torch.cuda.empty_cache()
+    vl_dw = BV.VocabLoss(R, V, d, row_list=True, head_grad=True, device=dev)
 
     def step_dw():
         dw.zero_()
-        vl(h, W, y, weights=wt, rows=rows_d, dh=dh, lse=lse, loss=loss, loss_sum=loss_sum, dw=dw)
+        vl_dw(h, W, y, weights=wt, rows=rows_d, dh=dh, lse=lse, loss=loss, loss_sum=loss_sum, dw=dw)
 
     for _ in range(args.warmup):
         step_dw()
@@ -444,7 +447,7 @@ def bench_vocab(args):
     with_dw = {"ms_per_step": round(ms_dw, 3), "loss_rows_per_s": round(R / (ms_dw * 1e-3), 1),
                "useful_tflops": round(6.0 * R * V * d / (ms_dw * 1e-3) / 1e12, 2),
                "kernels": {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof_dw.items()}}
-    del dw
+    del dw, vl_dw
     cpu = None
     if args.cpu_rows > 0:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbdvocab.
 
 BDVOCAB_OK, BDVOCAB_EINVAL, BDVOCAB_ENOTSUP, BDVOCAB_EHIP, BDVOCAB_EWORKSPACE, BDVOCAB_EBLAS = 0, -1, -2, -3, -4, -5
 BDVOCAB_BF16, BDVOCAB_F32 = 0, 1
+BDVOCAB_WS_ROW_LIST, BDVOCAB_WS_HEAD_GRAD = 1, 2
 
 EXPORTS = ("bdvocab_workspace_bytes", "bdvocab_loss", "bdvocab_status_string", "bdvocab_profile_enable",
            "bdvocab_profile_read")
@@ -78,8 +79,9 @@ def bdvocab_status_string(status):
     return lib().bdvocab_status_string(int(status)).decode()
 
 
-def bdvocab_workspace_bytes(prob, row_list):
-    return int(lib().bdvocab_workspace_bytes(C.byref(prob), 1 if row_list else 0))
+def bdvocab_workspace_bytes(prob, row_list, head_grad=False):
+    flags = (BDVOCAB_WS_ROW_LIST if row_list else 0) | (BDVOCAB_WS_HEAD_GRAD if head_grad else 0)
+    return int(lib().bdvocab_workspace_bytes(C.byref(prob), flags))
 
 
 def bdvocab_loss(prob, h, h_stride, w_head, rows, targets, weights, lse, loss, loss_sum, dh, dh_stride, dw,
@@ -109,10 +111,12 @@ def bdvocab_profile_read():
 class VocabLoss:
     """Owns the workspace for repeated calls of one problem shape."""
 
-    def __init__(self, n_rows, vocab, hidden, chunk=0, dh_dtype=BDVOCAB_BF16, row_list=False, device="cuda"):
+    def __init__(self, n_rows, vocab, hidden, chunk=0, dh_dtype=BDVOCAB_BF16, row_list=False, head_grad=False,
+                 device="cuda"):
         import torch
         self.prob = problem(n_rows, vocab, hidden, chunk, dh_dtype)
-        nbytes = bdvocab_workspace_bytes(self.prob, row_list)
+        nbytes = bdvocab_workspace_bytes(self.prob, row_list, head_grad)
+        self.head_grad = head_grad
         if nbytes == 0:
             raise BdvocabError(BDVOCAB_EINVAL, "bdvocab_workspace_bytes")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -127,6 +131,8 @@ class VocabLoss:
         R = self.prob.n_rows
         if (rows is not None) != self.row_list:
             raise ValueError("row list presence differs from the workspace's")
+        if dw is not None and not self.head_grad:
+            raise ValueError("dw needs a workspace made with head_grad=True")
         if loss is None:
             loss = torch.empty(R, dtype=torch.float32, device=h.device)
         bdvocab_loss(self.prob, h, h.stride(0), w_head, rows, targets, weights, lse, loss, loss_sum, dh,

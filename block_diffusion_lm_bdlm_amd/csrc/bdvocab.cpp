@@ -11,7 +11,8 @@
 //   rows          lse, loss, G = w (softmax - onehot) in bf16 over S
 //   grad GEMM     dH_chunk[n, d] = G W              (bf16 or fp32)
 //   (scatter)     packed dh rows -> their positions
-//   head GEMM     dW[V, d] += G^T H_chunk           (fp32, when requested)
+//   head GEMM     dW[V, d] += G^T H_chunk           (fp32, when requested; on
+//                 transposed copies of G and H_chunk, so that it too is TN)
 // In the GEMM library's column-major terms a row-major [r, c] matrix with
 // pitch p is a c x r matrix with leading dimension p, so the logits GEMM is
 // S^T (V x n) = op_T(W^T as d x V) * (H^T as d x n) and the gradient GEMM
@@ -58,7 +59,8 @@ int64_t logit_pitch(int32_t V) { return ((int64_t)V + 63) / 64 * 64; }
 struct Layout {
   int64_t chunk = 0;
   int64_t ld = 0;
-  size_t s_off = 0, wt_off = 0, hc_off = 0, dhc_off = 0, blas_off = 0, total = 0;
+  int64_t ldc = 0;  // row pitch of the transposed chunk copies (chunk rounded up to 64)
+  size_t s_off = 0, wt_off = 0, hc_off = 0, dhc_off = 0, gt_off = 0, ht_off = 0, blas_off = 0, total = 0;
 };
 
 int check_problem(const bdvocab_problem* p) {
@@ -69,7 +71,7 @@ int check_problem(const bdvocab_problem* p) {
   return BDVOCAB_OK;
 }
 
-Layout layout(const bdvocab_problem& p, bool row_list) {
+Layout layout(const bdvocab_problem& p, bool row_list, bool head_grad) {
   Layout L;
   int64_t c = p.chunk > 0 ? p.chunk : kDefaultChunk;
   c = std::min<int64_t>(c, std::max<int64_t>(p.n_rows, 1));
@@ -86,6 +88,13 @@ Layout layout(const bdvocab_problem& p, bool row_list) {
     off = round_up(off + (size_t)c * (size_t)p.hidden * 2, kAlign);
     L.dhc_off = off;
     off = round_up(off + (size_t)c * (size_t)p.hidden * es, kAlign);
+  }
+  L.ldc = (c + 63) / 64 * 64;
+  if (head_grad) {  // G^T [V, ldc] and H^T [d, ldc], bf16
+    L.gt_off = off;
+    off = round_up(off + (size_t)p.vocab * (size_t)L.ldc * 2, kAlign);
+    L.ht_off = off;
+    off = round_up(off + (size_t)p.hidden * (size_t)L.ldc * 2, kAlign);
   }
   L.blas_off = off;
   off += kBlasWs;
@@ -261,9 +270,10 @@ bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 // ===================================================================== ABI
 extern "C" {
 
-size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list) {
+size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int flags) {
   if (check_problem(problem) != BDVOCAB_OK) return 0;
-  return layout(*problem, row_list != 0).total;
+  if (flags & ~(BDVOCAB_WS_ROW_LIST | BDVOCAB_WS_HEAD_GRAD)) return 0;
+  return layout(*problem, (flags & BDVOCAB_WS_ROW_LIST) != 0, (flags & BDVOCAB_WS_HEAD_GRAD) != 0).total;
 }
 
 int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride, const void* w_head,
@@ -282,7 +292,7 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
     if (h_stride < d || h_stride % 8 != 0 || !aligned16(h) || !aligned16(w_head)) return BDVOCAB_EINVAL;
     if (dh && (dh_stride < d || (dh_stride * es) % 16 != 0 || !aligned16(dh))) return BDVOCAB_EINVAL;
     if (dw && !aligned16(dw)) return BDVOCAB_EINVAL;
-    const Layout L = layout(p, rows != nullptr);
+    const Layout L = layout(p, rows != nullptr, dw != nullptr);
     if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0 || ws_bytes < L.total)
       return BDVOCAB_EWORKSPACE;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -290,9 +300,11 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
     uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc_off);
     uint8_t* dhc = ws + L.dhc_off;
     uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.wt_off);
+    uint16_t* gt = reinterpret_cast<uint16_t*>(ws + L.gt_off);
+    uint16_t* ht = reinterpret_cast<uint16_t*>(ws + L.ht_off);
     void* blas_ws = ws + L.blas_off;
     if (dh) {
-      const TransposeArgs ta{static_cast<const uint16_t*>(w_head), p.vocab, (int32_t)d, wt, L.ld};
+      const TransposeArgs ta{static_cast<const uint16_t*>(w_head), p.vocab, (int32_t)d, d, wt, L.ld};
       const int rc = timed(K_TRANSPOSE, s, [&] { return hip_rc(launch_transpose(ta, s)); });
       if (rc != BDVOCAB_OK) return rc;
     }
@@ -330,9 +342,17 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
         }
       }
       if (dw) {
-        // dW^T (d x V) += (H^T as d x n) * op_T(G^T as V x n)
+        // G [n, V] (pitch 2 ld) -> G^T [V, ldc]; H_chunk [n, d] -> H^T [d, ldc]
+        const TransposeArgs tg{reinterpret_cast<const uint16_t*>(S), n, p.vocab, 2 * L.ld, gt, L.ldc};
+        const TransposeArgs th{static_cast<const uint16_t*>(Hb), n, (int32_t)d, ldh, ht, L.ldc};
+        rc = timed(K_TRANSPOSE, s, [&] {
+          const int r1 = hip_rc(launch_transpose(tg, s));
+          return r1 != BDVOCAB_OK ? r1 : hip_rc(launch_transpose(th, s));
+        });
+        if (rc != BDVOCAB_OK) return rc;
+        // dW^T (d x V) += op_T(H^T^T as n x d) * (G^T^T as n x V): both read along the rows
         rc = timed(K_HEAD, s, [&] {
-          return gemm(false, true, d, p.vocab, n, Hb, ldh, S, 2 * L.ld, dw, HIP_R_32F, d, blas_ws, s, true);
+          return gemm(true, false, d, p.vocab, n, ht, L.ldc, gt, L.ldc, dw, HIP_R_32F, d, blas_ws, s, true);
         });
         if (rc != BDVOCAB_OK) return rc;
       }

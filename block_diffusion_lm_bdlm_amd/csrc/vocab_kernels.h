@@ -60,11 +60,14 @@ struct ScatterArgs {
 };
 
 struct TransposeArgs {
-  const uint16_t* w;      // [V, d] bf16, pitch d
-  int64_t V;
-  int32_t d;              // multiple of 8
-  uint16_t* wt;           // [d, ldt] bf16
-  int64_t ldt;            // multiple of 8, >= V
+  const uint16_t* src;    // [rows, cols] 16-bit, row pitch src_pitch (a multiple of 8,
+                          // >= cols rounded up to 8: the last piece of a row may read pad)
+  int64_t rows;
+  int32_t cols;
+  int64_t src_pitch;
+  uint16_t* dst;          // [cols, rows] 16-bit, row pitch dst_pitch (a multiple of 8,
+                          // >= rows rounded up to 8; columns past rows get pad values)
+  int64_t dst_pitch;
 };
 
 hipError_t launch_rows(const RowsArgs& a, hipStream_t s);

@@ -316,23 +316,25 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   }
 }
 
-// Transposed copy of the head: W [V, d] (pitch d) -> Wt [d, V] (pitch ldt,
-// a multiple of 8 >= V).  One 64 x 64 tile per workgroup through LDS:
-// 16-byte loads along d, 16-byte stores along V; the row pitch of the LDS
-// tile is padded by two elements so that the column reads of the store
-// phase spread over the banks.  Pad columns [V, ldt) of Wt are left unset.
+// Transposed copy of a 16-bit matrix: src [rows, cols] -> dst [cols, rows]
+// (the head W [V, d] -> [d, V] for the gradient GEMM; a chunk's bf16 logit
+// gradient and hidden rows for the head GEMM).  One 64 x 64 tile per
+// workgroup through LDS: 16-byte loads along the source rows, 16-byte
+// stores along the destination rows; the LDS tile's row pitch is padded by
+// two elements so that the column reads of the store phase spread over the
+// banks.  Pad columns of dst past `rows` receive values that no reader uses.
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   __shared__ uint16_t tile[64][66];
-  const int64_t v0 = (int64_t)blockIdx.x * 64;
-  const int d0 = blockIdx.y * 64;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int piece = tid + 256 * k;  // 64 rows x 8 pieces of 8
+    const int piece = tid + 256 * k;  // 64 source rows x 8 pieces of 8
     const int r = piece >> 3, c = (piece & 7) * 8;
-    const int64_t v = v0 + r;
-    if (v < a.V && d0 + c < a.d) {
-      const uint4 x = *reinterpret_cast<const uint4*>(a.w + v * a.d + d0 + c);
+    const int64_t row = r0 + r;
+    if (row < a.rows && c0 + c < a.cols) {
+      const uint4 x = *reinterpret_cast<const uint4*>(a.src + row * a.src_pitch + c0 + c);
       const uint16_t* e = reinterpret_cast<const uint16_t*>(&x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) tile[r][c + i] = e[i];
@@ -341,15 +343,15 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int piece = tid + 256 * k;  // 64 output rows (d) x 8 pieces of 8 (V)
+    const int piece = tid + 256 * k;  // 64 destination rows (source columns) x 8 pieces of 8
     const int r = piece >> 3, c = (piece & 7) * 8;
-    const int dd = d0 + r;
-    const int64_t v = v0 + c;
-    if (dd < a.d && v < a.V) {
+    const int col = c0 + r;
+    const int64_t row = r0 + c;
+    if (col < a.cols && row < a.rows) {
       uint16_t e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) e[i] = tile[c + i][r];
-      *reinterpret_cast<uint4*>(a.wt + (int64_t)dd * a.ldt + v) = *reinterpret_cast<const uint4*>(e);
+      *reinterpret_cast<uint4*>(a.dst + (int64_t)col * a.dst_pitch + row) = *reinterpret_cast<const uint4*>(e);
     }
   }
 }
@@ -413,7 +415,8 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.V + 63) / 64), (unsigned)((a.d + 63) / 64));
+  if (a.rows <= 0 || a.cols <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.rows + 63) / 64), (unsigned)((a.cols + 63) / 64));
   hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

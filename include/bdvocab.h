@@ -30,7 +30,9 @@
  * workspace; one fused pass per row forms lse, the loss and the logit
  * gradient, written in bf16 over the same workspace rows; a second library
  * GEMM forms dh from a transposed copy of the head made once per call, and
- * a third, when dW is requested, adds the chunk's G^T H to dW.
+ * a third, when dW is requested, adds the chunk's G^T H to dW (from
+ * transposed copies of G and H, so that both operands run along the
+ * contraction).
  * Device memory for logits is C * V * 4 bytes, never R * V.  The first call
  * of a shape times the GEMM library's candidate algorithms on the call's
  * stream (synchronising that call) and keeps the fastest; BDVOCAB_TUNE=0
@@ -79,10 +81,13 @@ typedef struct {
 
 /* Bytes of device workspace bdvocab_loss needs for `problem` (256-byte
  * aligned base required): the chunk's logits, the transposed head, and the
- * GEMM library's 64 MiB.  `row_list` != 0 when the call passes a row index
- * list (adds the gathered chunk of hidden rows and of dh).  Returns 0 for an
- * invalid problem. */
-size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list);
+ * GEMM library's 64 MiB.  `flags`: BDVOCAB_WS_ROW_LIST when the call passes
+ * a row index list (adds the gathered chunk of hidden rows and of dh);
+ * BDVOCAB_WS_HEAD_GRAD when it passes dw (adds transposed copies of a
+ * chunk's logit gradient and hidden rows, V x C and d x C bf16).  Returns 0
+ * for an invalid problem or unknown flag bits. */
+enum { BDVOCAB_WS_ROW_LIST = 1, BDVOCAB_WS_HEAD_GRAD = 2 };
+size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int flags);
 
 /* Loss, lse and dh of the R loss rows.
  *   h        bf16, device.  Row r is read at h + idx_r * h_stride elements,
@@ -107,7 +112,8 @@ size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int row_list);
  *            library's first algorithm (never the timing search, whose runs
  *            would accumulate).
  *   workspace / ws_bytes: at least bdvocab_workspace_bytes(problem,
- *            rows != NULL); the contents need not be initialised.
+ *            (rows ? BDVOCAB_WS_ROW_LIST : 0) | (dw ? BDVOCAB_WS_HEAD_GRAD
+ *            : 0)); the contents need not be initialised.
  * R = 0 enqueues only the zeroing of loss_sum. */
 int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride,
                  const void* w_head, const int32_t* rows, const int32_t* targets,

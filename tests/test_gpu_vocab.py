@@ -54,7 +54,7 @@ def _run(dev, seed, T, R, V, d, chunk, row_list, dh_dtype, weighted=True, ignore
         wt = (0.1 + 1.9 * torch.rand(R, generator=g)).to(dev)
     for i, val in ignored:
         y[i] = val
-    vl = BV.VocabLoss(R, V, d, chunk=chunk, dh_dtype=dh_dtype, row_list=row_list, device=dev)
+    vl = BV.VocabLoss(R, V, d, chunk=chunk, dh_dtype=dh_dtype, row_list=row_list, head_grad=head_grad, device=dev)
     out_dt = torch.float32 if dh_dtype == BV.BDVOCAB_F32 else torch.bfloat16
     dh = torch.full((T, d), SENTINEL, dtype=out_dt, device=dev)
     lse = torch.empty(R, dtype=torch.float32, device=dev)

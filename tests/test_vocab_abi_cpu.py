@@ -31,17 +31,23 @@ def _up(x, a=256):
     return (x + a - 1) // a * a
 
 
-@pytest.mark.parametrize("R,V,d,chunk,dt,rows", [(32768, 131072, 5120, 0, 0, True), (300, 5000, 256, 128, 1, False),
-                                                 (5, 7, 8, 0, 0, True), (0, 10, 8, 0, 0, False)])
-def test_workspace_layout(R, V, d, chunk, dt, rows):
+@pytest.mark.parametrize("R,V,d,chunk,dt,rows,hg", [(32768, 131072, 5120, 0, 0, True, True),
+                                                    (300, 5000, 256, 128, 1, False, False),
+                                                    (300, 5000, 256, 100, 1, False, True),
+                                                    (5, 7, 8, 0, 0, True, False), (0, 10, 8, 0, 0, False, True)])
+def test_workspace_layout(R, V, d, chunk, dt, rows, hg):
     c = min(chunk if chunk > 0 else 8192, max(R, 1))
     ld = (V + 63) // 64 * 64
     es = 4 if dt == BV.BDVOCAB_F32 else 2
     want = _up(c * ld * 4) + _up(d * ld * 2)
     if rows:
         want += _up(c * d * 2) + _up(c * d * es)
+    if hg:
+        ldc = (c + 63) // 64 * 64
+        want += _up(V * ldc * 2) + _up(d * ldc * 2)
     want += 64 << 20
-    assert BV.bdvocab_workspace_bytes(BV.problem(R, V, d, chunk, dt), rows) == want
+    assert BV.bdvocab_workspace_bytes(BV.problem(R, V, d, chunk, dt), rows, hg) == want
+    assert BV.lib().bdvocab_workspace_bytes(BV.problem(R, V, d, chunk, dt), 4) == 0  # unknown flag bit
 
 
 def _status(*a):
@@ -90,6 +96,8 @@ def test_invalid_arguments_rejected_on_host():
     assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, None, small) == BV.BDVOCAB_EWORKSPACE
     assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, None, _Fake((1 << 20) + 16, ws_need)) \
         == BV.BDVOCAB_EWORKSPACE
+    # a head gradient needs the larger workspace
+    assert _status(p, h, 64, w, None, y, None, None, loss, None, None, 0, _Fake(28672), ws) == BV.BDVOCAB_EWORKSPACE
     # a row list needs the larger workspace
     assert _status(p, h, 64, w, _Fake(24576), y, None, None, loss, None, None, 0, None, ws) == BV.BDVOCAB_EWORKSPACE
     # no rows and no loss sum: nothing to do, no HIP call
