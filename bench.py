@@ -486,7 +486,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS) + sorted(VOCAB_WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle sample size (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--report-all", action="store_true",
