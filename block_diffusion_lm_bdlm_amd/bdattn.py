@@ -13,6 +13,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbdattn.so")
 
 BDATTN_OK, BDATTN_EINVAL, BDATTN_ENOTSUP, BDATTN_EHIP, BDATTN_EWORKSPACE = 0, -1, -2, -3, -4
+BDATTN_ERANGE = -5
 BDATTN_BF16, BDATTN_F32 = 0, 1
 BDATTN_CLEAN_BLOCK_CAUSAL, BDATTN_CLEAN_TOKEN_CAUSAL = 0, 1
 BDATTN_BWD_DELTA_READY, BDATTN_BWD_OVERWRITE = 1, 2
@@ -47,9 +48,10 @@ class BdattnError(RuntimeError):
 
 
 _lib = None
-EXPORTS = ("bdattn_assign_blocks", "bdattn_clean_shard", "bdattn_plan_order",
+EXPORTS = ("bdattn_assign_blocks", "bdattn_clean_shard", "bdattn_plan_order", "bdattn_plan_order_keys",
            "bdattn_workspace_bytes", "bdattn_fwd", "bdattn_shard_merge", "bdattn_bwd",
-           "bdattn_status_string", "bdattn_profile_enable", "bdattn_profile_read")
+           "bdattn_workspace_status", "bdattn_status_string", "bdattn_profile_enable",
+           "bdattn_profile_read")
 
 
 def lib():
@@ -63,6 +65,8 @@ def lib():
     L.bdattn_assign_blocks.argtypes = [i32, i32, i32, P(C.c_int32)]
     L.bdattn_clean_shard.argtypes = [i32, i32, i32, P(KV)]
     L.bdattn_plan_order.argtypes = [P(Problem), P(Share), P(KV), P(C.c_int32), i64, P(C.c_int64)]
+    L.bdattn_plan_order_keys.argtypes = [P(Problem), P(Share), P(KV), P(C.c_int32), i64, P(C.c_int64)]
+    L.bdattn_workspace_status.argtypes = [vp, vp]
     L.bdattn_workspace_bytes.argtypes = [P(Problem), P(Share), P(KV), C.c_int]
     L.bdattn_workspace_bytes.restype = C.c_size_t
     L.bdattn_fwd.argtypes = [P(Problem), P(Share), P(KV)] + [Tensor] * 7 + [i32, vp, vp, C.c_size_t, vp]
@@ -151,15 +155,32 @@ def bdattn_clean_shard(L, P, s):
     return out
 
 
-def bdattn_plan_order(prob, sh, kvs):
+def _order(fn, name, prob, sh, kvs):
     n = C.c_int64(0)
-    _check(lib().bdattn_plan_order(C.byref(prob), C.byref(sh), C.byref(kvs), None, 0, C.byref(n)),
-           "bdattn_plan_order")
+    _check(fn(C.byref(prob), C.byref(sh), C.byref(kvs), None, 0, C.byref(n)), name)
     items = np.zeros(4 * n.value, dtype=np.int32)
-    _check(lib().bdattn_plan_order(C.byref(prob), C.byref(sh), C.byref(kvs),
-                                   items.ctypes.data_as(C.POINTER(C.c_int32)), items.size, C.byref(n)),
-           "bdattn_plan_order")
+    _check(fn(C.byref(prob), C.byref(sh), C.byref(kvs), items.ctypes.data_as(C.POINTER(C.c_int32)), items.size,
+              C.byref(n)), name)
     return items.reshape(-1, 4)
+
+
+def bdattn_plan_order(prob, sh, kvs):
+    """Query-major order: rows (batch, query head, tile, tile or -1)."""
+    return _order(lib().bdattn_plan_order, "bdattn_plan_order", prob, sh, kvs)
+
+
+def bdattn_plan_order_keys(prob, sh, kvs):
+    """Key-major order: rows (batch, KV head, key tile, key tile or -1)."""
+    return _order(lib().bdattn_plan_order_keys, "bdattn_plan_order_keys", prob, sh, kvs)
+
+
+def bdattn_workspace_status(workspace, stream=None):
+    """BDATTN_OK or BDATTN_ERANGE for the last call that used ``workspace``
+    (synchronises the stream); raises on other errors."""
+    st = lib().bdattn_workspace_status(_p(workspace), _stream(stream))
+    if st not in (BDATTN_OK, BDATTN_ERANGE):
+        _check(st, "bdattn_workspace_status")
+    return st
 
 
 def bdattn_workspace_bytes(prob, sh, kvs, bwd):

@@ -160,11 +160,18 @@ struct Carve {
   }
 };
 
+// Every bf16 workspace starts with a 256-byte header whose first int32 is
+// the call's range flag (cleared by the call, set by the packing kernels
+// when a value converted to fp16 lies outside the half range).
+constexpr size_t kHeaderBytes = 256;
+
 struct FwdWs {
+  int32_t* flag;
   uint16_t* kn;
   _Float16* vt;
 };
 struct BwdWs {
+  int32_t* flag;
   _Float16 *kh, *vh;
   _Float16 *qh, *doh;
   float *lse2, *dc;
@@ -176,6 +183,7 @@ size_t carve_fwd(const Plan& P, bool f32, char* base, FwdWs* w) {
   if (f32) return 0;
   const size_t nk = (size_t)P.batch * P.hkv * P.nkc * P.d;
   FwdWs t;
+  t.flag = cv.take<int32_t>(kHeaderBytes / 4);
   t.kn = cv.take<uint16_t>(nk);
   t.vt = cv.take<_Float16>(nk);
   if (w) *w = t;
@@ -188,6 +196,7 @@ size_t carve_bwd(const Plan& P, char* base, BwdWs* w) {
   const size_t nq = (size_t)P.batch * P.hq * P.nqc * P.d;
   const size_t nr = (size_t)P.batch * P.hq * P.nqc;
   BwdWs t;
+  t.flag = cv.take<int32_t>(kHeaderBytes / 4);
   t.kh = cv.take<_Float16>(nk);
   t.vh = cv.take<_Float16>(nk);
   t.qh = cv.take<_Float16>(nq);
@@ -211,8 +220,8 @@ bool tensor_ok(const bdattn_tensor& t, int elem_bytes) {
 TensorArg targ(const bdattn_tensor& t) { return TensorArg{t.ptr, t.batch_stride, t.row_stride, t.head_stride}; }
 
 // ------------------------------------------------------------------ profiling
-enum Kind { K_PACK_K, K_PACK_Q, K_FWD, K_FWD_F32, K_DQ, K_DKDV, K_MERGE, K_COUNT };
-const char* kKindNames[K_COUNT] = {"pack_k", "pack_q", "fwd_bf16", "fwd_f32", "dq", "dkdv", "merge"};
+enum Kind { K_PACK_K, K_PACK_Q, K_FWD, K_FWD_F32, K_DQ, K_DKDV, K_MERGE, K_FLAG, K_COUNT };
+const char* kKindNames[K_COUNT] = {"pack_k", "pack_q", "fwd_bf16", "fwd_f32", "dq", "dkdv", "merge", "flag_clear"};
 
 struct Prof {
   std::mutex mu;
@@ -265,6 +274,7 @@ const char* bdattn_status_string(int status) {
     case BDATTN_ENOTSUP: return "not supported";
     case BDATTN_EHIP: return "HIP runtime error";
     case BDATTN_EWORKSPACE: return "workspace missing or too small";
+    case BDATTN_ERANGE: return "an input value lies outside the fp16 range (clamped)";
     default: return "unknown status";
   }
 }
@@ -312,6 +322,26 @@ int bdattn_plan_order(const bdattn_problem* problem, const bdattn_share* share, 
   return BDATTN_OK;
 }
 
+int bdattn_plan_order_keys(const bdattn_problem* problem, const bdattn_share* share, const bdattn_kv* kv,
+                           int32_t* items, int64_t cap, int64_t* n) {
+  int32_t runs = 0;
+  if (!n || !problem_ok(problem) || !share_ok(problem, share, &runs) || !kv_ok(problem, kv))
+    return BDATTN_EINVAL;
+  const Plan P = make_plan(problem, share, kv);
+  *n = P.nwg_k;
+  if (items) {
+    if (cap < 4 * P.nwg_k) return BDATTN_EINVAL;
+    for (int64_t w = 0; w < P.nwg_k; ++w) {
+      const WgK wg = decode_wg_k(P, w);
+      items[4 * w + 0] = wg.b;
+      items[4 * w + 1] = wg.g;
+      items[4 * w + 2] = wg.tile_a;
+      items[4 * w + 3] = wg.tile_b;
+    }
+  }
+  return BDATTN_OK;
+}
+
 size_t bdattn_workspace_bytes(const bdattn_problem* problem, const bdattn_share* share,
                               const bdattn_kv* kv, int bwd) {
   int32_t runs = 0;
@@ -321,10 +351,16 @@ size_t bdattn_workspace_bytes(const bdattn_problem* problem, const bdattn_share*
   return need;
 }
 
-int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share, const bdattn_kv* kv,
-               bdattn_tensor q_clean, bdattn_tensor q_corr, bdattn_tensor k_clean, bdattn_tensor v_clean,
-               bdattn_tensor k_corr, bdattn_tensor v_corr, bdattn_tensor o, int32_t o_dtype, float* lse,
-               void* workspace, size_t ws_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace bd {
+
+// Body of bdattn_fwd: validation, then the packing and forward kernels on
+// the given scratch of `ws_bytes` bytes.
+int fwd_impl(const bdattn_problem* problem, const bdattn_share* share, const bdattn_kv* kv,
+             bdattn_tensor q_clean, bdattn_tensor q_corr, bdattn_tensor k_clean, bdattn_tensor v_clean,
+             bdattn_tensor k_corr, bdattn_tensor v_corr, bdattn_tensor o, int32_t o_dtype, float* lse,
+             void* workspace, size_t ws_bytes, void* hip_stream) {
   int32_t runs = 0;
   if (!problem_ok(problem) || !share_ok(problem, share, &runs) || !kv_ok(problem, kv)) return BDATTN_EINVAL;
   if (!problem_supported(problem)) return BDATTN_ENOTSUP;
@@ -363,6 +399,8 @@ int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share, const b
   }
   FwdWs ws;
   carve_fwd(P, false, static_cast<char*>(workspace), &ws);
+  hipError_t e = timed(K_FLAG, s, [&] { return launch_flag_clear(ws.flag, s); });
+  if (e != hipSuccess) return BDATTN_EHIP;
   PackKArgs pk;
   std::memset(&pk, 0, sizeof pk);
   pk.k_clean = targ(k_clean);
@@ -371,7 +409,8 @@ int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share, const b
   pk.v_corr = targ(v_corr);
   pk.kn = ws.kn;
   pk.vt = ws.vt;
-  hipError_t e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
+  pk.flag = ws.flag;
+  e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   FwdArgs a;
   a.q_clean = targ(q_clean);
@@ -385,6 +424,28 @@ int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share, const b
   a.o_f32 = o_dtype == BDATTN_F32;
   a.lse = lse;
   return hip_status(timed(K_FWD, s, [&] { return launch_fwd_bf16(P, a, s); }));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share, const bdattn_kv* kv,
+               bdattn_tensor q_clean, bdattn_tensor q_corr, bdattn_tensor k_clean, bdattn_tensor v_clean,
+               bdattn_tensor k_corr, bdattn_tensor v_corr, bdattn_tensor o, int32_t o_dtype, float* lse,
+               void* workspace, size_t ws_bytes, void* hip_stream) {
+  return fwd_impl(problem, share, kv, q_clean, q_corr, k_clean, v_clean, k_corr, v_corr, o, o_dtype, lse,
+                  workspace, ws_bytes, hip_stream);
+}
+
+int bdattn_workspace_status(const void* workspace, void* hip_stream) {
+  const void* ws = workspace;
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return BDATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  int32_t flag = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return BDATTN_EHIP;
+  if (hipMemcpy(&flag, ws, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess) return BDATTN_EHIP;
+  return flag ? BDATTN_ERANGE : BDATTN_OK;
 }
 
 int bdattn_shard_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc, const float* o_part,
@@ -439,11 +500,13 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   BwdWs ws;
   carve_bwd(P, static_cast<char*>(workspace), &ws);
+  hipError_t e = timed(K_FLAG, s, [&] { return launch_flag_clear(ws.flag, s); });
+  if (e != hipSuccess) return BDATTN_EHIP;
   // pack_q also forms D = rowsum(dO * O) unless the caller gives it
   PackQArgs pq{targ(q_clean), targ(q_corr), targ(d_o), delta_ready ? TensorArg{} : targ(o_final),
                o_dtype == BDATTN_F32, delta_ready != 0, lse_final, delta, ws.qh, ws.doh,
-               ws.lse2, ws.dc, ws.vis};
-  hipError_t e = timed(K_PACK_Q, s, [&] { return launch_pack_q(P, pq, s); });
+               ws.lse2, ws.dc, ws.vis, ws.flag};
+  e = timed(K_PACK_Q, s, [&] { return launch_pack_q(P, pq, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   if (P.nkc == 0) return BDATTN_OK;  // no key in this call: nothing to add
   PackKArgs pk;
@@ -454,6 +517,7 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   pk.v_corr = targ(v_corr);
   pk.kh = ws.kh;
   pk.vh = ws.vh;
+  pk.flag = ws.flag;
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kh, ws.vh,

@@ -69,12 +69,22 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float((uint32_t)u << 16);
 }
 
-// Eight bf16 values (as loaded, two per dword) to fp16 through fp32; exact
-// for values in the half range above its subnormals.
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4& v) {
+// Largest finite fp16 value.
+constexpr float kHalfMax = 65504.f;
+
+// Eight bf16 values (as loaded, two per dword), times `mul` (a power of two),
+// to fp16 through fp32 with round-to-nearest-even: exact for products in
+// the half range above its subnormals.  A product outside [-65504, 65504]
+// (or NaN) sets `bad`; finite ones are clamped to the half range.
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4& v, float mul, bool& bad) {
   f16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (_Float16)bf16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+  for (int e = 0; e < 8; ++e) {
+    float x = bf16_to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1)))) * mul;
+    bad |= !(fabsf(x) <= kHalfMax);
+    if (fabsf(x) > kHalfMax) x = copysignf(kHalfMax, x);
+    r[e] = (_Float16)x;
+  }
   return r;
 }
 

@@ -25,6 +25,7 @@ struct PackKArgs {
   _Float16* kh;   // natural K in fp16 (nullable)
   _Float16* vh;   // natural V in fp16 (nullable)
   _Float16* vt;   // transposed V (nullable)
+  int32_t* flag;  // set to 1 when a value converted to fp16 lies outside its range
 };
 
 // Compact query space: the share's query segments back to back, segment s
@@ -38,10 +39,12 @@ struct PackQArgs {
   float* delta;        // [batch][R][hq]
   _Float16* qh;        // [batch][hq][nqc][d] fp16: the bf16 values in half precision
   _Float16* doh;
-  float* lse2;         // [batch][hq][nqc] log2-scaled LSE; +inf on padding rows
-  float* dc;           // [batch][hq][nqc] delta; 0 on padding rows
+  float* lse2;         // [batch][hq][nqc] log2 LSE - c (row_pscale); +inf on padding rows
+  float* dc;           // [batch][hq][nqc] D * 2^-c; 0 on padding rows
+  // qh: Q in fp16; doh: dO * 2^-c in fp16 (c = the row's row_pscale)
   int32_t* vis;        // [4][nqc] visible source rows per compact row: [lo, hi) of the
                        // clean keys, then [lo, hi) of the packed corrupted keys; 0 on padding
+  int32_t* flag;       // set to 1 when a value converted to fp16 lies outside its range
 };
 
 struct FwdArgs {
@@ -97,6 +100,7 @@ struct MergeArgs {
   uint16_t* o_bf16;
 };
 
+hipError_t launch_flag_clear(int32_t* flag, hipStream_t s);
 hipError_t launch_pack_k(const Plan& P, const PackKArgs& a, hipStream_t s);
 hipError_t launch_pack_q(const Plan& P, const PackQArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s);

@@ -13,9 +13,13 @@
 //          gives D, it is formed here from the dO row being packed and the
 //          final O: D_i = sum_t dO_i[t] O_i[t], the softmax backward's row
 //          term, and stored for later calls.
-// Both are bandwidth-bound copies; neither changes a value except the
-// bf16 -> fp16 conversions (exact for values in the half range and above
-// its subnormals).
+// Both are bandwidth-bound copies.  The bf16 -> fp16 conversions are exact
+// for values in the half range above its subnormals; a value outside the
+// half range is clamped to it and raises the call's range flag.  pack_q
+// also applies each row's probability scale 2^-c (row_pscale): dO and D are
+// stored times 2^-c and log2 LSE minus c, so the backward kernels form
+// P * 2^c, which stays out of fp16's subnormal range on long rows, while
+// every product they accumulate keeps its value.
 #include "device.h"
 #include "kernels.h"
 
@@ -31,12 +35,24 @@ struct __attribute__((aligned(16))) PackSmem {
   uint16_t b[kPT][D + 8];  // bf16 rows of V (16-byte aligned)
 };
 
-__device__ inline _Float16 bf16_to_f16(uint16_t u) { return (_Float16)bf16_to_f32(u); }
+// bf16 -> fp16, clamped to the half range; `bad` records a value outside it.
+__device__ inline _Float16 bf16_to_f16(uint16_t u, bool& bad) {
+  float x = bf16_to_f32(u);
+  bad |= !(fabsf(x) <= kHalfMax);
+  if (fabsf(x) > kHalfMax) x = copysignf(kHalfMax, x);
+  return (_Float16)x;
+}
+
+// Records an out-of-range conversion in the call's flag word (a plain
+// vector store; every writer stores the same value).
+__device__ inline void raise_flag(int32_t* flag, bool bad) {
+  if (bad) *reinterpret_cast<volatile int32_t*>(flag) = 1;
+}
 
 
 // Writes the transposed, perm16-ordered fp16 tile [D][kPT] (contiguous) from LDS rows.
 template <int D>
-__device__ inline void store_transposed(const uint16_t (*rows)[D + 8], _Float16* out, int tid) {
+__device__ inline void store_transposed(const uint16_t (*rows)[D + 8], _Float16* out, int tid, bool& bad) {
   constexpr int ld = kPT;
   // each thread writes 8 consecutive slots (16 bytes) of one output row
   for (int ch = tid; ch < D * (kPT / 8); ch += 256) {
@@ -46,7 +62,7 @@ __device__ inline void store_transposed(const uint16_t (*rows)[D + 8], _Float16*
     for (int e = 0; e < 8; ++e) {
       const int slot = s0 + e;
       const int key = (slot & ~15) + perm16(slot & 15);
-      v[e] = bf16_to_f16(rows[key][d]);
+      v[e] = bf16_to_f16(rows[key][d], bad);
     }
     *reinterpret_cast<f16x8*>(out + (int64_t)d * ld + s0) = v;
   }
@@ -64,6 +80,7 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
   const KSeg K = P.k[j];
   const TensorArg& KT = K.kind == KIND_CLEAN ? A.k_clean : A.k_corr;
   const TensorArg& VT = K.kind == KIND_CLEAN ? A.v_clean : A.v_corr;
+  bool bad = false;
   for (int ch = tid; ch < kPT * (D / 8); ch += 256) {
     const int r = ch / (D / 8), dc = (ch % (D / 8)) * 8;
     const int32_t cc = c + r;
@@ -75,15 +92,16 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const Plan P, const PackKAr
     }
     const int64_t nat = ((int64_t)(b * P.hkv + g) * P.nkc + cc) * D + dc;
     if (A.kn) *reinterpret_cast<u32x4*>(A.kn + nat) = kv;
-    if (A.kh) *reinterpret_cast<f16x8*>(A.kh + nat) = bf16x8_to_f16x8(kv);
-    if (A.vh) *reinterpret_cast<f16x8*>(A.vh + nat) = bf16x8_to_f16x8(vv);
+    if (A.kh) *reinterpret_cast<f16x8*>(A.kh + nat) = bf16x8_to_f16x8(kv, 1.f, bad);
+    if (A.vh) *reinterpret_cast<f16x8*>(A.vh + nat) = bf16x8_to_f16x8(vv, 1.f, bad);
     *reinterpret_cast<u32x4*>(&sm.b[r][dc]) = vv;
   }
   if (A.vt) {
     __syncthreads();
     const int64_t tb = (int64_t)(b * P.hkv + g) * D * P.nkc + (int64_t)c * D;  // tile c / kPT
-    store_transposed<D>(sm.b, A.vt + tb, tid);
+    store_transposed<D>(sm.b, A.vt + tb, tid, bad);
   }
+  raise_flag(A.flag, bad);
 }
 
 // OM: how D = rowsum(dO * O) is obtained: kDeltaGiven (read from A.delta),
@@ -136,6 +154,7 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
         }
       }
     }
+    bool bad = false;
 #pragma unroll
     for (int it = 0; it < kIter; ++it) {
       const int ch = tid + 256 * it;
@@ -144,6 +163,9 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
         qv[it] = u32x4{0, 0, 0, 0};
         dv[it] = u32x4{0, 0, 0, 0};
       }
+      // this row's probability scale: dO is stored times 2^-c
+      const int32_t cs = row_pscale(row_nkeys(row_bounds(P, S, min(rbase + r, last))));
+      const float dscale = __int_as_float((127 - cs) << 23);
       float dd = 0.f;  // this chunk's part of D
       if constexpr (OM != kDeltaGiven) {
         float ov[8];
@@ -166,9 +188,10 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
         if (dc == 0) dsum[r] = dd;
       }
       const int64_t nat = (hb * P.nqc + c + r) * D + dc;
-      *reinterpret_cast<f16x8*>(A.qh + nat) = bf16x8_to_f16x8(qv[it]);
-      *reinterpret_cast<f16x8*>(A.doh + nat) = bf16x8_to_f16x8(dv[it]);
+      *reinterpret_cast<f16x8*>(A.qh + nat) = bf16x8_to_f16x8(qv[it], 1.f, bad);
+      *reinterpret_cast<f16x8*>(A.doh + nat) = bf16x8_to_f16x8(dv[it], dscale, bad);
     }
+    raise_flag(A.flag, bad);
     __syncthreads();  // dsum
     if (tid < kPT) {
       const int32_t rr = rbase + tid;
@@ -176,15 +199,18 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
       if (rr < S.nrows) {
         const int64_t idx = ((int64_t)b * P.R + S.row0 + rr) * P.hq + h;
         const float lse = A.lse[idx];
+        const int32_t cs = row_pscale(row_nkeys(row_bounds(P, S, rr)));
         // a row that sees no key (LSE = -inf) has O = 0 and no gradient: +inf
-        // makes every recomputed probability exp2(s - inf) vanish.
-        l2 = lse == -INFINITY ? INFINITY : lse * 1.4426950408889634f;
+        // makes every recomputed probability exp2(s - inf) vanish.  Otherwise
+        // log2 LSE - c, so the kernels' exp2(s log2 e - lse2) is P * 2^c.
+        l2 = lse == -INFINITY ? INFINITY : lse * 1.4426950408889634f - (float)cs;
         if constexpr (OM == kDeltaGiven) {
           dd = A.delta[idx];
         } else {
           dd = dsum[tid];
           A.delta[idx] = dd;
         }
+        dd *= __int_as_float((127 - cs) << 23);  // D * 2^-c, like the row's dO
       }
       A.lse2[hb * P.nqc + c + tid] = l2;
       A.dc[hb * P.nqc + c + tid] = dd;
@@ -207,7 +233,16 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
   }
 }
 
+__global__ void flag_clear_kernel(int32_t* flag) {
+  if (threadIdx.x == 0) *reinterpret_cast<volatile int32_t*>(flag) = 0;
+}
+
 }  // namespace
+
+hipError_t launch_flag_clear(int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_k(const Plan& P, const PackKArgs& a, hipStream_t s) {
   if (P.nkc == 0) return hipSuccess;

@@ -167,6 +167,26 @@ __host__ __device__ inline int32_t clampi(int32_t x, int32_t lo, int32_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
+// Number of keys a row sees in the whole mask (every key of every call):
+// its clean interval plus, for a corrupted row, its own block.
+__host__ __device__ inline int32_t row_nkeys(const RowBounds& rb) {
+  const int32_t nc = rb.hi_clean > rb.lo_clean ? rb.hi_clean - rb.lo_clean : 0;
+  return nc + (rb.hi_loc - rb.lo_loc);
+}
+
+// Probability scale of a backward row: the kernels form P * 2^c instead of
+// P, with dO and D of the row packed as dO * 2^-c and D * 2^-c, so every
+// product (P dO, P (dP - D)) keeps its value while P leaves fp16's
+// subnormal range.  A row that sees n keys has probabilities of order 1/n;
+// c = ceil(log2 n) - 7, within [0, 15], lifts them to about 2^-7, and
+// P * 2^c <= 2^15 holds for any row (P <= 1).
+constexpr int32_t kPScaleBias = 7;
+constexpr int32_t kPScaleMax = 15;
+__host__ __device__ inline int32_t row_pscale(int32_t n) {
+  const int32_t lg = n <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(n - 1));  // ceil(log2 n)
+  return clampi(lg - kPScaleBias, 0, kPScaleMax);
+}
+
 // Row's visible compact interval [vlo, vhi) within key segment ks.
 __host__ __device__ inline void compact_range(const KSeg& ks, const RowBounds& rb, bool clean_row,
                                               int32_t* vlo, int32_t* vhi) {

@@ -50,8 +50,14 @@
  * Tensors.  bdattn_tensor gives a base pointer (device memory) and strides
  * in elements for batch, row and head; the head dimension d is contiguous.
  * dtype BDATTN_BF16 or BDATTN_F32 as stated per argument.  Values of bf16
- * inputs must lie within the IEEE half range (|x| < 65504): products with
- * probabilities run in fp16 matrix cores.
+ * inputs must lie within the IEEE half range (|x| <= 65504): products with
+ * probabilities run in fp16 matrix cores, on operands converted from bf16
+ * (exact in that range).  A value outside it (or NaN) is clamped to the
+ * range (NaN stays NaN) and raises the call's range flag, which
+ * bdattn_workspace_status reports as BDATTN_ERANGE; such a call's results
+ * are not those of the inputs.  The backward also needs each per-pair term
+ * |dO_i . v_j - D_i| below 65504 * 2^c_i (c_i the row's probability scale,
+ * see bdattn_bwd).
  *
  * Conventions for every entry point.
  *   - Device buffers are caller-owned; the library allocates no device
@@ -81,7 +87,8 @@ typedef enum bdattn_status {
   BDATTN_EINVAL = -1,     /* invalid argument                          */
   BDATTN_ENOTSUP = -2,    /* valid but not supported (dtype, d, ...)    */
   BDATTN_EHIP = -3,       /* a HIP runtime call or launch failed        */
-  BDATTN_EWORKSPACE = -4  /* workspace NULL or smaller than required    */
+  BDATTN_EWORKSPACE = -4, /* workspace NULL or smaller than required    */
+  BDATTN_ERANGE = -5      /* an input value lay outside the fp16 range  */
 } bdattn_status;
 
 typedef enum bdattn_dtype { BDATTN_BF16 = 0, BDATTN_F32 = 1 } bdattn_dtype;
@@ -167,6 +174,23 @@ int bdattn_plan_order(const bdattn_problem* problem, const bdattn_share* share,
                       const bdattn_kv* kv, int32_t* items, int64_t cap,
                       int64_t* n);
 
+/* Workgroup work order of the key-major backward kernel (dK/dV) for this
+ * call (bit-exact contract), by the same dual-end rule applied to key tiles
+ * ([P1] "负载均衡：为什么要首尾块配对"; [P3] "Load balancing: pairing early
+ * and late blocks"): for each workgroup in dispatch order, four int32 values
+ * (batch, KV head, first key tile, second key tile or -1).  Key tiles hold
+ * 128 keys of one key segment: the call's clean ranges in order, then its
+ * corrupted keys, each segment starting a new tile.  Clean tile t (counted
+ * over the clean segments) is paired with clean tile n-1-t, the earlier one
+ * first, so each workgroup's two tiles together are seen by the same number
+ * of query rows wherever the rows seeing a key fall linearly with its
+ * position (the whole mask); tiles of corrupted keys, each seen only by its
+ * own block's rows, are single.  `cap`, `*n` as in bdattn_plan_order.
+ * Pure host function. */
+int bdattn_plan_order_keys(const bdattn_problem* problem,
+                           const bdattn_share* share, const bdattn_kv* kv,
+                           int32_t* items, int64_t cap, int64_t* n);
+
 /* Workspace bytes for one bdattn_fwd (bwd = 0) or bdattn_bwd (bwd = 1) call
  * with these arguments; 0 on invalid arguments. */
 size_t bdattn_workspace_bytes(const bdattn_problem* problem,
@@ -188,6 +212,14 @@ int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share,
                int32_t o_dtype, float* lse, void* workspace, size_t ws_bytes,
                void* hip_stream);
 
+/* Range flag of the last bf16 bdattn_fwd / bdattn_bwd call that used
+ * `workspace` (device pointer, as passed to that call).  Synchronises
+ * `hip_stream` (the stream of that call), then returns BDATTN_ERANGE if
+ * that call clamped an input value to the fp16 range, else BDATTN_OK
+ * (BDATTN_EINVAL for a NULL or misaligned workspace, BDATTN_EHIP on a HIP
+ * error). */
+int bdattn_workspace_status(const void* workspace, void* hip_stream);
+
 /* Log-sum-exp merge of a partial result into an accumulator, in fp32
  * ([P1] "在线 softmax 合并", equations for m, w1, w2, O and z; numerator,
  * max and normaliser kept in fp32 to the last step):
@@ -207,6 +239,10 @@ int bdattn_shard_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
  * fused backward").  The softmax is the FINAL one: o_final and lse_final
  * are the merged forward results over every key the rows see, so the
  * per-call contributions of a sharded key set sum to the full gradient.
+ * Precision: the kernels form each probability as P * 2^c_i and the row's
+ * dO and D times 2^-c_i (c_i = ceil(log2 n_i) - 7 within [0, 15], n_i the
+ * number of keys row i sees in the whole mask), which keeps P out of fp16's
+ * subnormal range on long rows and leaves every product unchanged.
  *   q_*, k_*, v_*: as in bdattn_fwd (bf16 only).
  *   o_final: share rows x hq, o_dtype BDATTN_BF16 or BDATTN_F32; read only
  *          when D is formed here (flags without BDATTN_BWD_DELTA_READY),

@@ -143,3 +143,41 @@ def test_delta_rowsum(dev, d, o_f32):
     torch.cuda.synchronize()
     for a, b in zip(first, grads[:5]):
         assert torch.equal(a, b)
+
+
+def test_range_flag(dev, orc):
+    """Inputs outside the fp16 range: the call clamps them, raises its range
+    flag (bdattn_workspace_status -> BDATTN_ERANGE) and keeps the forward
+    finite; the next call on the same workspace with in-range inputs
+    clears it.  In-range inputs leave it clear and match the oracle."""
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd.runner import WholeMask
+    from tests.common import doubled_inputs, host_bits
+    batch, L, M, hq, hkv, d = 1, 256, 16, 4, 2, 128
+    q, k, v, do = doubled_inputs(501, batch, L, hq, hkv, d, device=dev)
+    wm = WholeMask(batch, L, M, hq, hkv, d)
+    wsf, wsb = wm.workspace(False, dev), wm.workspace(True, dev)
+    o, lse = wm.fwd(q, k, v, o_dtype=torch.float32, ws=wsf)
+    assert B.bdattn_workspace_status(wsf) == B.BDATTN_OK
+    wm.bwd(q, k, v, o, lse, do, ws=wsb)
+    assert B.bdattn_workspace_status(wsb) == B.BDATTN_OK
+    p = orc.problem(batch, L, M, hq, hkv, d, bf16=True)
+    ro, rl = orc.fwd(p, orc.keys(), *(host_bits(x) for x in (q, k, v)))
+    assert max_abs(o.cpu().numpy(), ro) <= TOL_O and max_abs(lse.cpu().numpy(), rl) <= TOL_LSE
+    print("[range] in-range call: flag clear, O and LSE within tolerance", flush=True)
+    # V (converted to fp16 by the forward's packing) out of range
+    vb = v.clone()
+    vb[0, 3, 1, 7] = 1.0e6
+    o2, _ = wm.fwd(q, k, vb, o_dtype=torch.float32, ws=wsf)
+    assert B.bdattn_workspace_status(wsf) == B.BDATTN_ERANGE
+    assert torch.isfinite(o2).all()
+    # K (converted by the backward's packing) out of range
+    kb = k.clone()
+    kb[0, 5, 0, 3] = -7.0e4
+    wm.bwd(q, kb, v, o, lse, do, ws=wsb)
+    assert B.bdattn_workspace_status(wsb) == B.BDATTN_ERANGE
+    # the flag belongs to the last call on the workspace
+    wm.fwd(q, k, v, o_dtype=torch.float32, ws=wsf)
+    assert B.bdattn_workspace_status(wsf) == B.BDATTN_OK
+    wm.bwd(q, k, v, o, lse, do, ws=wsb)
+    assert B.bdattn_workspace_status(wsb) == B.BDATTN_OK
