@@ -32,6 +32,12 @@ WORKLOADS = {
     "bdlm_L8K_M32_b2_h16kv8_d128": (2, 8192, 32, 16, 8, 128),
 }
 DEFAULT = "bdlm_L64K_M32_h40kv8_d128"
+# One GPU's CSBP share: name -> (seed index, L, M, hq, hkv, P, clean-shard
+# query rows, outlier fraction); rank 0, d = 128.
+CSBP_WORKLOADS = {
+    "csbp_L256K_P8_r0_h32kv8_d128": (3, 262144, 32, 32, 8, 8, False, 0.0),
+    "csbp_L512K_M16_P16_r0_h32kv4_d128": (4, 524288, 16, 32, 4, 16, True, 0.01),
+}
 VOCAB_WORKLOADS = {
     # name: (L corrupted positions, block size M, hidden d, vocabulary V)
     "vocab_L64K_M32_d5120_V131072": (65536, 32, 5120, 131072),
@@ -210,6 +216,59 @@ def share_pairs(L, M, blocks, clean_q):
     return n
 
 
+def csbp_setup(name, dev):
+    """Inputs, buffers and one-step closure of a CSBP share workload: the
+    local call, P zigzag shard calls each followed by an LSE merge, then the
+    backward over the local keys and every shard (accumulators zeroed first,
+    as the first call of a step needs).  Returns a dict with the step, the
+    useful FLOPs per step and the merge's algorithmic bytes per step."""
+    import torch
+
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    from block_diffusion_lm_bdlm_amd import synth
+    from block_diffusion_lm_bdlm_amd.runner import CsbpShare
+
+    idx, L, M, hq, hkv, P, clean_queries, outl = CSBP_WORKLOADS[name]
+    d = 128
+    blocks = B.bdattn_assign_blocks(L // M, P, 0).tolist()
+    cs = B.bdattn_clean_shard(L, P, 0)
+    clean_q = [(cs.lo[0], cs.hi[0]), (cs.lo[1], cs.hi[1])] if clean_queries else []
+    shards = []
+    for s_ in range(P):
+        kk = B.bdattn_clean_shard(L, P, s_)
+        shards.append([(kk.lo[0], kk.hi[0]), (kk.lo[1], kk.hi[1])])
+    seed = synth.SEED_BASE + idx
+    n_clean = sum(hi - lo for lo, hi in clean_q)
+    nx = len(blocks) * M
+    f = dict(device=dev, outlier_frac=outl)
+    qc = synth.normal((1, max(n_clean, 1), hq, d), seed, "q_clean", **f)[:, :n_clean]
+    qx = synth.normal((1, nx, hq, d), seed, "q_corr", **f)
+    kx = synth.normal((1, nx, hkv, d), seed, "k_corr", **f)
+    vx = synth.normal((1, nx, hkv, d), seed, "v_corr", **f)
+    kc = synth.normal((1, L, hkv, d), seed, "k", **f)
+    vc = synth.normal((1, L, hkv, d), seed, "v", **f)
+    sh = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, shards)
+    do = synth.normal((1, sh.R, hq, d), seed, "do", dev)
+    wf, wb = sh.workspace(False, dev), sh.workspace(True, dev)
+    grads = sh.alloc_grads(dev)
+
+    def step(mid=None):
+        o32, lse, _ = sh.fwd(qc, qx, kc, vc, kx, vx, ws=wf)
+        if mid is not None:
+            mid.record()
+        for g_ in grads[:5]:
+            g_.zero_()
+        sh.bwd(qc, qx, kc, vc, kx, vx, o32, lse, do, ws=wb, grads=grads)
+
+    # merge: per merged row, read two (O, LSE) partials and write one in fp32,
+    # plus the bf16 O of the last merge: P merges of R * hq rows per step
+    mrows = sh.R * hq
+    return {"step": step, "flops": 14 * d * share_pairs(L, M, blocks, clean_q) * hq, "L": L, "M": M, "P": P,
+            "hq": hq, "hkv": hkv, "d": d, "R": sh.R, "blocks": len(blocks), "clean_q": clean_q,
+            "merge_bytes": P * mrows * 3 * (4 * d + 4) + mrows * 2 * d,
+            "merge_rows_per_launch": mrows}
+
+
 def report_all(reps=3):
     """Times every benchmark workload (stderr table, one JSON line per
     workload on stdout).  Not the headline line: that is the default run."""
@@ -272,46 +331,12 @@ def report_all(reps=3):
         del q, k, v, do, wm, wf, wb, grads, state
         torch.cuda.empty_cache()
     merge_bytes = {}
-    shares = [("csbp_L256K_P8_r0_h32kv8", 3, 262144, 32, 32, 8, 8, False, 0.0),
-              ("csbp_L512K_P16_r0_h32kv4_outliers", 4, 524288, 16, 32, 4, 16, True, 0.01)]
-    for name, idx, L, M, hq, hkv, P, clean_queries, outl in shares:
-        d = 128
-        blocks = B.bdattn_assign_blocks(L // M, P, 0).tolist()
-        cs = B.bdattn_clean_shard(L, P, 0)
-        clean_q = [(cs.lo[0], cs.hi[0]), (cs.lo[1], cs.hi[1])] if clean_queries else []
-        shards = []
-        for s_ in range(P):
-            kk = B.bdattn_clean_shard(L, P, s_)
-            shards.append([(kk.lo[0], kk.hi[0]), (kk.lo[1], kk.hi[1])])
-        seed = synth.SEED_BASE + idx
-        n_clean = sum(hi - lo for lo, hi in clean_q)
-        nx = len(blocks) * M
-        f = dict(device=dev, outlier_frac=outl)
-        qc = synth.normal((1, max(n_clean, 1), hq, d), seed, "q_clean", **f)[:, :n_clean]
-        qx = synth.normal((1, nx, hq, d), seed, "q_corr", **f)
-        kx = synth.normal((1, nx, hkv, d), seed, "k_corr", **f)
-        vx = synth.normal((1, nx, hkv, d), seed, "v_corr", **f)
-        kc = synth.normal((1, L, hkv, d), seed, "k", **f)
-        vc = synth.normal((1, L, hkv, d), seed, "v", **f)
-        sh = CsbpShare(1, L, M, hq, hkv, d, blocks, clean_q, shards)
-        do = synth.normal((1, sh.R, hq, d), seed, "do", dev)
-        wf, wb = sh.workspace(False, dev), sh.workspace(True, dev)
-        grads = sh.alloc_grads(dev)
-
-        def step():
-            o32, lse, _ = sh.fwd(qc, qx, kc, vc, kx, vx, ws=wf)
-            for g_ in grads[:5]:
-                g_.zero_()
-            sh.bwd(qc, qx, kc, vc, kx, vx, o32, lse, do, ws=wb, grads=grads)
-
-        ms, kern = timed(step)
-        flops = 14 * d * share_pairs(L, M, blocks, clean_q) * hq
-        # merge: per merged row, read two (O, LSE) partials and write one in fp32, plus
-        # the bf16 O of the last merge: P merges of R * hq rows per step
-        mrows = sh.R * hq
-        merge_bytes[name] = P * mrows * 3 * (4 * d + 4) + mrows * 2 * d
-        rows.append((name, ms, flops, L // P, kern))
-        del qc, qx, kx, vx, kc, vc, sh, do, wf, wb, grads
+    for name in CSBP_WORKLOADS:
+        cs_ = csbp_setup(name, dev)
+        ms, kern = timed(cs_["step"])
+        merge_bytes[name] = cs_["merge_bytes"]
+        rows.append((name, ms, cs_["flops"], cs_["L"] // cs_["P"], kern))
+        del cs_
         torch.cuda.empty_cache()
     print(f"{'workload':36s} {'ms':>9s} {'useful TF/s':>12s} {'% of 2.5PF':>10s} {'tokens/s':>12s}",
           file=sys.stderr)
@@ -480,12 +505,88 @@ def bench_vocab(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_csbp(args):
+    """One GPU's CSBP share: P shard calls merged by LSE and the sharded
+    backward, timed per step; the dominant kernel's MFMA roofline and the
+    LSE merge's HBM roofline (algorithmic bytes per launch over its average
+    launch time)."""
+    import torch
+
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating inputs for {args.workload}", file=sys.stderr, flush=True)
+    cs = csbp_setup(args.workload, dev)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        cs["step"]()
+    torch.cuda.synchronize()
+    B.bdattn_profile_read()
+    B.bdattn_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        marks[i][0].record()
+        cs["step"](marks[i][1])
+        marks[i][2].record()
+    e1.record()
+    torch.cuda.synchronize()
+    B.bdattn_profile_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = B.bdattn_profile_read()
+    print(f"[bench] {args.steps} steps, {ms:.2f} ms/step; kernels: "
+          + ", ".join(f"{n} {c}x {t / c:.3f} ms" for n, (c, t) in sorted(prof.items(), key=lambda x: -x[1][1])),
+          file=sys.stderr, flush=True)
+    tflops = cs["flops"] / (ms * 1e-3) / 1e12
+    dom_name, (dom_cnt, dom_ms) = max(prof.items(), key=lambda kv_: kv_[1][1])
+    dom_avg = dom_ms / dom_cnt
+    # the share's useful FLOPs of the dominant kernel per step, spread over its launches
+    per_pair = {"fwd_bf16": 4, "dkdv": 8, "dq": 2}.get(dom_name)
+    roof = None
+    if per_pair is not None:
+        ach = per_pair / 14.0 * cs["flops"] / dom_cnt * args.steps / (dom_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(dom_avg, 3)}
+    merge = None
+    if "merge" in prof:
+        mc, mt = prof["merge"]
+        per_launch = cs["merge_bytes"] / cs["P"]  # the last merge also writes bf16 O: averaged in
+        gbs = per_launch / (mt / mc * 1e-3) / 1e9
+        merge = {"bound": "hbm", "kernel": "merge", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": int(per_launch),
+                 "rows_per_launch": cs["merge_rows_per_launch"], "avg_ms": round(mt / mc, 4)}
+    step_ms = [m[0].elapsed_time(m[2]) for m in marks]
+    out = {
+        "metric": "useful attention TFLOP/s fwd+bwd of one GPU's CSBP share (1 GPU); % of bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic N(0,1) bf16 inputs, seeded",
+        "config": {"workload": args.workload, "L": cs["L"], "M": cs["M"], "P": cs["P"], "rank": 0,
+                   "blocks": cs["blocks"], "share_rows": cs["R"], "clean_query_ranges": cs["clean_q"],
+                   "hq": cs["hq"], "hkv": cs["hkv"], "d": cs["d"], "parallelism": "single GPU"},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(cs["L"] / cs["P"] / (ms * 1e-3), 1),
+        "step_ms": {"median": round(float(np.median(step_ms)), 3), "min": round(min(step_ms), 3),
+                    "max": round(max(step_ms), 3)},
+        "fwd_ms_median": round(float(np.median([m[0].elapsed_time(m[1]) for m in marks])), 3),
+        "bwd_ms_median": round(float(np.median([m[1].elapsed_time(m[2]) for m in marks])), 3),
+        "kernels": {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof.items()},
+        "roofline": roof,
+        "merge_roofline": merge,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS) + sorted(VOCAB_WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT,
+                    choices=sorted(WORKLOADS) + sorted(CSBP_WORKLOADS) + sorted(VOCAB_WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle sample size (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (counter calibration) and exit")
@@ -505,6 +606,9 @@ def main():
 
     if args.workload in VOCAB_WORKLOADS:
         bench_vocab(args)
+        return
+    if args.workload in CSBP_WORKLOADS:
+        bench_csbp(args)
         return
 
     import torch

@@ -53,9 +53,10 @@ def _flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + _flags() + EXTRA.get(src, [])
+def _compile(src, build_dir=BUILD, host_flags=()):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    host = [x for f in host_flags for x in ("-Xarch_host", f)]
+    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + _flags() + EXTRA.get(src, []) + host
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -85,6 +86,22 @@ def build(verbose=False):
     _link([results[x][0] for x in SOURCES], LIB)
     _link([results[x][0] for x in VOCAB_SOURCES], VOCAB_LIB, VOCAB_LINK)
     return LIB
+
+
+def build_sanitized(out_dir, sanitizers=("address", "undefined")):
+    """libbdattn.so with the host code built under the given sanitizers
+    (device code unchanged), into out_dir, for the CPU sanitizer job: the
+    host planner, argument validation and workspace carving run under
+    AddressSanitizer / UndefinedBehaviorSanitizer there.  The library then
+    needs the clang sanitizer runtime preloaded."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = ["-fsanitize=" + ",".join(sanitizers), "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        results = list(ex.map(lambda x: _compile(x, out_dir, flags), SOURCES))
+    out = os.path.join(out_dir, "libbdattn.so")
+    host_link = [x for f in flags for x in ("-Xarch_host", f)] + ["-shared-libsan"]
+    _link([r[0] for r in results], out, host_link)
+    return out
 
 
 if __name__ == "__main__":

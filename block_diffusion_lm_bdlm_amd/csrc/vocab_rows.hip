@@ -326,33 +326,36 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   __shared__ uint16_t tile[64][66];
   const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
+  // column tiles stride by gridDim.y, which the launch caps at 65535
+  for (int64_t c0 = (int64_t)blockIdx.y * 64; c0 < a.cols; c0 += (int64_t)gridDim.y * 64) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int piece = tid + 256 * k;  // 64 source rows x 8 pieces of 8
-    const int r = piece >> 3, c = (piece & 7) * 8;
-    const int64_t row = r0 + r;
-    if (row < a.rows && c0 + c < a.cols) {
-      const uint4 x = *reinterpret_cast<const uint4*>(a.src + row * a.src_pitch + c0 + c);
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&x);
+    for (int k = 0; k < 2; ++k) {
+      const int piece = tid + 256 * k;  // 64 source rows x 8 pieces of 8
+      const int r = piece >> 3, c = (piece & 7) * 8;
+      const int64_t row = r0 + r;
+      if (row < a.rows && c0 + c < a.cols) {
+        const uint4 x = *reinterpret_cast<const uint4*>(a.src + row * a.src_pitch + c0 + c);
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&x);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) tile[r][c + i] = e[i];
+        for (int i = 0; i < 8; ++i) tile[r][c + i] = e[i];
+      }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int piece = tid + 256 * k;  // 64 destination rows (source columns) x 8 pieces of 8
-    const int r = piece >> 3, c = (piece & 7) * 8;
-    const int col = c0 + r;
-    const int64_t row = r0 + c;
-    if (col < a.cols && row < a.rows) {
-      uint16_t e[8];
+    for (int k = 0; k < 2; ++k) {
+      const int piece = tid + 256 * k;  // 64 destination rows (source columns) x 8 pieces of 8
+      const int r = piece >> 3, c = (piece & 7) * 8;
+      const int64_t col = c0 + r;
+      const int64_t row = r0 + c;
+      if (col < a.cols && row < a.rows) {
+        uint16_t e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = tile[c + i][r];
-      *reinterpret_cast<uint4*>(a.dst + (int64_t)col * a.dst_pitch + row) = *reinterpret_cast<const uint4*>(e);
+        for (int i = 0; i < 8; ++i) e[i] = tile[c + i][r];
+        *reinterpret_cast<uint4*>(a.dst + col * a.dst_pitch + row) = *reinterpret_cast<const uint4*>(e);
+      }
     }
+    __syncthreads();  // the next column tile reuses the LDS tile
   }
 }
 
@@ -416,7 +419,8 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
   if (a.rows <= 0 || a.cols <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.rows + 63) / 64), (unsigned)((a.cols + 63) / 64));
+  const int64_t ct = (a.cols + 63) / 64;
+  const dim3 grid((unsigned)((a.rows + 63) / 64), (unsigned)(ct < 65535 ? ct : 65535));
   hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

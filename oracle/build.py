@@ -22,5 +22,19 @@ def build(force=True):
     return LIB
 
 
+def build_sanitized(out_dir, sanitizers=("address", "undefined")):
+    """The oracle under the given sanitizers, built with the ROCm clang so
+    that it shares one sanitizer runtime with the sanitized libbdattn (CPU
+    sanitizer job; OpenMP off, so the runtime sees plain threads)."""
+    os.makedirs(out_dir, exist_ok=True)
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+    out = os.path.join(out_dir, "libbdoracle.so")
+    cmd = [clang, "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fsanitize=" + ",".join(sanitizers), "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-shared-libsan", "-o", out, os.path.join(HERE, "bdoracle.c"), "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build())

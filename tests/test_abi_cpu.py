@@ -176,3 +176,19 @@ def test_bwd_flags_rejected_on_host():
     assert st(whole_s, whole_k, 4) == B.BDATTN_EINVAL
     # the whole-mask call passes the flag check and fails later on its missing tensors
     assert st(whole_s, whole_k, B.BDATTN_BWD_OVERWRITE | B.BDATTN_BWD_DELTA_READY) == B.BDATTN_EINVAL
+
+
+def test_sanitized_libraries_loaded():
+    """Under the CPU sanitizer job (BDATTN_SANITIZED_DIR set), the sanitized
+    libbdattn and oracle are the ones mapped, with the sanitizer runtime."""
+    d = os.environ.get("BDATTN_SANITIZED_DIR")
+    if not d:
+        pytest.skip("not the sanitizer job")
+    from oracle import oracle as orc
+    B.lib()
+    orc.lib()
+    maps = open("/proc/self/maps").read()
+    assert os.path.join(d, "libbdattn.so") in maps
+    assert os.path.join(d, "libbdoracle.so") in maps
+    assert "libclang_rt.asan" in maps
+    print("sanitized libraries mapped")

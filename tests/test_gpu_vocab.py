@@ -195,3 +195,12 @@ def test_vocab_full_size_sampled(dev):
     # a few positions that carry no loss are untouched
     free = np.setdiff1d(np.arange(0, L, 997), rows.numpy())[:8]
     assert torch.all(dh[torch.as_tensor(free, device=dev).long()] == SENTINEL)
+
+
+def test_vocab_head_grad_vocabulary_past_transpose_grid(dev):
+    """A vocabulary of more than 65535 column tiles of 64 (V > 4,194,240):
+    the chunk's gradient transpose for the head GEMM strides its column
+    tiles over the capped grid, so the head gradient covers every row of the
+    vocabulary."""
+    V = 65535 * 64 + 3 * 64 + 5
+    _check(_run(dev, 41, 12, 6, V, 8, 4, True, 0, head_grad=True))
