@@ -13,7 +13,8 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbdattn.so")
 
 BDATTN_OK, BDATTN_EINVAL, BDATTN_ENOTSUP, BDATTN_EHIP, BDATTN_EWORKSPACE = 0, -1, -2, -3, -4
-BDATTN_ERANGE = -5
+BDATTN_ERANGE, BDATTN_ESCRATCH = -5, -6
+BDATTN_STATIC_SCRATCH_BYTES = 256 << 20
 BDATTN_BF16, BDATTN_F32 = 0, 1
 BDATTN_CLEAN_BLOCK_CAUSAL, BDATTN_CLEAN_TOKEN_CAUSAL = 0, 1
 BDATTN_BWD_DELTA_READY, BDATTN_BWD_OVERWRITE = 1, 2
@@ -49,7 +50,7 @@ class BdattnError(RuntimeError):
 
 _lib = None
 EXPORTS = ("bdattn_assign_blocks", "bdattn_clean_shard", "bdattn_plan_order", "bdattn_plan_order_keys",
-           "bdattn_workspace_bytes", "bdattn_fwd", "bdattn_shard_merge", "bdattn_bwd",
+           "bdattn_workspace_bytes", "bdattn_fwd", "bdattn_fwd_static", "bdattn_shard_merge", "bdattn_bwd",
            "bdattn_workspace_status", "bdattn_status_string", "bdattn_profile_enable",
            "bdattn_profile_read")
 
@@ -70,6 +71,7 @@ def lib():
     L.bdattn_workspace_bytes.argtypes = [P(Problem), P(Share), P(KV), C.c_int]
     L.bdattn_workspace_bytes.restype = C.c_size_t
     L.bdattn_fwd.argtypes = [P(Problem), P(Share), P(KV)] + [Tensor] * 7 + [i32, vp, vp, C.c_size_t, vp]
+    L.bdattn_fwd_static.argtypes = [P(Problem), P(Share), P(KV)] + [Tensor] * 7 + [i32, vp, vp]
     L.bdattn_shard_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp]
     L.bdattn_bwd.argtypes = ([P(Problem), P(Share), P(KV)] + [Tensor] * 7 + [i32, vp, Tensor, vp, i32]
                              + [vp] * 5 + [vp, C.c_size_t, vp])
@@ -194,6 +196,15 @@ def bdattn_fwd(prob, sh, kvs, q_clean, q_corr, k_clean, v_clean, k_corr, v_corr,
                                    tensor(k_clean), tensor(v_clean), tensor(k_corr), tensor(v_corr),
                                    tensor(o), o_dtype, _p(lse), _p(workspace), ws_bytes, _stream(stream)),
                   "bdattn_fwd")
+
+
+def bdattn_fwd_static(prob, sh, kvs, q_clean, q_corr, k_clean, v_clean, k_corr, v_corr, o, o_dtype, lse,
+                      stream=None):
+    """bdattn_fwd with the library's static device scratch (no workspace)."""
+    return _check(lib().bdattn_fwd_static(C.byref(prob), C.byref(sh), C.byref(kvs), tensor(q_clean),
+                                          tensor(q_corr), tensor(k_clean), tensor(v_clean), tensor(k_corr),
+                                          tensor(v_corr), tensor(o), o_dtype, _p(lse), _stream(stream)),
+                  "bdattn_fwd_static")
 
 
 def bdattn_shard_merge(rows, d, o_acc, lse_acc, o_part, lse_part, o_final_bf16=None, stream=None):

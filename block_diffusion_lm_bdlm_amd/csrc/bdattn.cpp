@@ -9,6 +9,7 @@
 #include <mutex>
 #include <vector>
 
+#include "abi_internal.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -275,6 +276,7 @@ const char* bdattn_status_string(int status) {
     case BDATTN_EHIP: return "HIP runtime error";
     case BDATTN_EWORKSPACE: return "workspace missing or too small";
     case BDATTN_ERANGE: return "an input value lies outside the fp16 range (clamped)";
+    case BDATTN_ESCRATCH: return "problem needs more scratch than the static buffer holds";
     default: return "unknown status";
   }
 }
@@ -440,7 +442,11 @@ int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share, const b
 
 int bdattn_workspace_status(const void* workspace, void* hip_stream) {
   const void* ws = workspace;
-  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256) return BDATTN_EINVAL;
+  if (!ws) {  // the static scratch of bdattn_fwd_static on the current device
+    ws = static_scratch_ptr();
+    if (!ws) return BDATTN_EHIP;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return BDATTN_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   int32_t flag = 0;
   if (hipStreamSynchronize(s) != hipSuccess) return BDATTN_EHIP;

@@ -88,7 +88,9 @@ typedef enum bdattn_status {
   BDATTN_ENOTSUP = -2,    /* valid but not supported (dtype, d, ...)    */
   BDATTN_EHIP = -3,       /* a HIP runtime call or launch failed        */
   BDATTN_EWORKSPACE = -4, /* workspace NULL or smaller than required    */
-  BDATTN_ERANGE = -5      /* an input value lay outside the fp16 range  */
+  BDATTN_ERANGE = -5,     /* an input value lay outside the fp16 range  */
+  BDATTN_ESCRATCH = -6    /* bdattn_fwd_static: problem needs more than
+                             BDATTN_STATIC_SCRATCH_BYTES of scratch      */
 } bdattn_status;
 
 typedef enum bdattn_dtype { BDATTN_BF16 = 0, BDATTN_F32 = 1 } bdattn_dtype;
@@ -212,11 +214,33 @@ int bdattn_fwd(const bdattn_problem* problem, const bdattn_share* share,
                int32_t o_dtype, float* lse, void* workspace, size_t ws_bytes,
                void* hip_stream);
 
+/* Forward with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and results as
+ * bdattn_fwd; the scratch bdattn_fwd takes from `workspace` comes instead
+ * from a static device buffer of BDATTN_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  Problems
+ * whose bdattn_workspace_bytes(..., 0) exceed it return BDATTN_ESCRATCH
+ * before any device work.  The call allocates nothing (its first call on a
+ * device looks up the buffer's address once).  Every call on one GPU uses
+ * the same buffer: calls that overlap on one GPU (concurrent streams or
+ * threads) race and must be serialised by the caller; calls on one stream
+ * are ordered.  bdattn_workspace_status(NULL, stream) reads its range
+ * flag. */
+#define BDATTN_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int bdattn_fwd_static(const bdattn_problem* problem, const bdattn_share* share,
+                      const bdattn_kv* kv, bdattn_tensor q_clean,
+                      bdattn_tensor q_corr, bdattn_tensor k_clean,
+                      bdattn_tensor v_clean, bdattn_tensor k_corr,
+                      bdattn_tensor v_corr, bdattn_tensor o, int32_t o_dtype,
+                      float* lse, void* hip_stream);
+
 /* Range flag of the last bf16 bdattn_fwd / bdattn_bwd call that used
- * `workspace` (device pointer, as passed to that call).  Synchronises
+ * `workspace` (device pointer, as passed to that call; NULL: the last
+ * bdattn_fwd_static call on the current device).  Synchronises
  * `hip_stream` (the stream of that call), then returns BDATTN_ERANGE if
  * that call clamped an input value to the fp16 range, else BDATTN_OK
- * (BDATTN_EINVAL for a NULL or misaligned workspace, BDATTN_EHIP on a HIP
+ * (BDATTN_EINVAL for a misaligned workspace, BDATTN_EHIP on a HIP
  * error). */
 int bdattn_workspace_status(const void* workspace, void* hip_stream);
 

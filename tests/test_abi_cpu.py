@@ -178,6 +178,21 @@ def test_bwd_flags_rejected_on_host():
     assert st(whole_s, whole_k, B.BDATTN_BWD_OVERWRITE | B.BDATTN_BWD_DELTA_READY) == B.BDATTN_EINVAL
 
 
+def test_static_forward_oversize_rejected_on_host():
+    """bdattn_fwd_static rejects a problem whose forward scratch exceeds
+    BDATTN_STATIC_SCRATCH_BYTES before any HIP call (no GPU here)."""
+    L = 65536
+    p = B.problem(1, L, 32, 40, 8, 128)
+    s = B.share(range(L // 32), [(0, L)])
+    k = B.kv([(0, L)], True)
+    assert B.bdattn_workspace_bytes(p, s, k, 0) > B.BDATTN_STATIC_SCRATCH_BYTES
+    assert _status(B.bdattn_fwd_static, p, s, k, *([None] * 7), B.BDATTN_BF16, None, 0) == B.BDATTN_ESCRATCH
+    assert B.bdattn_status_string(B.BDATTN_ESCRATCH).startswith("problem needs more scratch")
+    # an invalid problem is reported as such, also before any HIP call
+    bad = B.problem(1, 1000, 16, 4, 2, 128)
+    assert _status(B.bdattn_fwd_static, bad, s, k, *([None] * 7), B.BDATTN_BF16, None, 0) == B.BDATTN_EINVAL
+
+
 def test_sanitized_libraries_loaded():
     """Under the CPU sanitizer job (BDATTN_SANITIZED_DIR set), the sanitized
     libbdattn and oracle are the ones mapped, with the sanitizer runtime."""
