@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
 VOCAB_LIB = os.path.join(HERE, "libbdvocab.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["bdattn.cpp", "static_fwd.cpp", "fwd.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
+SOURCES = ["bdattn.cpp", "static_fwd.cpp", "fwd.hip", "fwd_f32.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
 VOCAB_SOURCES = ["bdvocab.cpp", "vocab_rows.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 VOCAB_LINK = ["-L", os.path.join(ROCM, "lib"), "-lhipblaslt", "-Wl,-rpath," + os.path.join(ROCM, "lib")]

@@ -244,106 +244,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const Plan P, const Fw
   }
 }
 
-// ------------------------------------------------------------------ fp32
-// Exact-precision path for fp32 inputs: two lanes per query row (lane l and
-// l+32 each own half of d), scores from LDS-staged fp32 K tiles on the
-// vector ALUs, the same online softmax, V accumulated in fp32.
-template <int D>
-struct __attribute__((aligned(16))) F32Smem {
-  float k[kBK][D + 1];
-  float v[kBK][D + 1];
-};
-
-template <int D>
-__device__ void fwd_f32_tile(const Plan& P, const FwdF32Args& A, F32Smem<D>& sm, int b, int h, int g,
-                             int32_t tile) {
-  constexpr int DH = D / 2;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
-  const QSeg S = P.q[seg_of_tile(P, tile)];
-  const int32_t r0 = (tile - S.tile0) * kBQ;
-  const int32_t n = min(kBQ, S.nrows - r0);
-  const int32_t rq = wave * 32 + ql;
-  const int32_t rc = min(rq, n - 1);
-  const bool clean = S.kind == KIND_CLEAN;
-  const TensorArg& QT = clean ? A.q_clean : A.q_corr;
-  const float* qp = static_cast<const float*>(QT.p) + b * QT.bs + (int64_t)(S.src0 + r0 + rc) * QT.rs +
-                    (int64_t)h * QT.hs + hh * DH;
-  float q[DH], o[DH];
-#pragma unroll
-  for (int t = 0; t < DH; ++t) {
-    q[t] = qp[t];
-    o[t] = 0.f;
-  }
-  const RowBounds rb = row_bounds(P, S, r0 + rc);
-  const KeyWalk w = keywalk_build(P, S, r0, r0 + n - 1);
-  float m_run = -INFINITY, l_run = 0.f;
-  for (int32_t t = 0; t < w.total; ++t) {
-    int32_t c, ri;
-    bool full;
-    keywalk_at(w, t, &c, &ri, &full);
-    const KSeg K = P.k[ri];
-    const TensorArg& KT = K.kind == KIND_CLEAN ? A.k_clean : A.k_corr;
-    const TensorArg& VT = K.kind == KIND_CLEAN ? A.v_clean : A.v_corr;
-    __syncthreads();
-    for (int e = tid; e < kBK * D; e += 256) {
-      const int key = e / D, dd = e % D;
-      const int32_t cc = c + key;
-      float kv = 0.f, vv = 0.f;
-      if (cc < K.c0 + K.len) {
-        const int64_t row = K.t0 + (cc - K.c0);
-        kv = static_cast<const float*>(KT.p)[b * KT.bs + row * KT.rs + (int64_t)g * KT.hs + dd];
-        vv = static_cast<const float*>(VT.p)[b * VT.bs + row * VT.rs + (int64_t)g * VT.hs + dd];
-      }
-      sm.k[key][dd] = kv;
-      sm.v[key][dd] = vv;
-    }
-    __syncthreads();
-    int32_t vlo, vhi;
-    compact_range(K, rb, clean, &vlo, &vhi);
-    float s[kBK];
-    float mx = -INFINITY;
-    for (int key = 0; key < kBK; ++key) {
-      float acc = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < DH; ++t2) acc = fmaf(q[t2], sm.k[key][hh * DH + t2], acc);
-      acc += __shfl_xor(acc, 32, 64);
-      const int32_t cc = c + key;
-      s[key] = (cc >= vlo && cc < vhi) ? acc * P.scale : -INFINITY;
-      mx = fmaxf(mx, s[key]);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = expf(m_run - m_use);
-    l_run *= alpha;
-#pragma unroll
-    for (int t2 = 0; t2 < DH; ++t2) o[t2] *= alpha;
-    for (int key = 0; key < kBK; ++key) {
-      const float p = expf(s[key] - m_use);
-      l_run += p;
-#pragma unroll
-      for (int t2 = 0; t2 < DH; ++t2) o[t2] = fmaf(p, sm.v[key][hh * DH + t2], o[t2]);
-    }
-    m_run = m_new;
-  }
-  if (rq < n) {
-    const int32_t row = S.row0 + r0 + rq;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = A.o + b * A.o_bs + (int64_t)row * A.o_rs + (int64_t)h * A.o_hs + hh * DH;
-#pragma unroll
-    for (int t2 = 0; t2 < DH; ++t2) op[t2] = o[t2] * inv;
-    if (hh == 0)
-      A.lse[((int64_t)b * P.R + row) * P.hq + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void fwd_f32_kernel(const Plan P, const FwdF32Args A) {
-  __shared__ F32Smem<D> sm;
-  const WgQ wg = decode_wg_q(P, blockIdx.x);
-  fwd_f32_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);
-  if (wg.tile_b >= 0) fwd_f32_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_b);
-}
-
 }  // namespace
 
 hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s) {
@@ -352,15 +252,6 @@ hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
   else
     hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_fwd_f32(const Plan& P, const FwdF32Args& a, hipStream_t s) {
-  if (P.nwg_q == 0) return hipSuccess;
-  if (P.d == 128)
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
-  else
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -141,9 +141,14 @@ __device__ __forceinline__ f16x8 tr_frag(const _Float16* step, const LaneOff<D>&
 // acc += A B with the accumulator held in AGPRs for the whole walk.  The
 // product is written as inline assembly so the accumulator stays in the
 // AGPRs while every other product (compiled in the VGPR form) feeds vector
-// code directly.  Inputs come from LDS reads and vector instructions, whose
-// results the hardware interlocks for the matrix core; the accumulator is
-// read back only after agpr_settle().
+// code directly.  The compiler places no wait states around inline
+// assembly.  Operands loaded from LDS are covered by the waitcnt the
+// compiler emits for the asm's inputs; operands written by vector
+// instructions are not interlocked for the matrix core and need the fenced
+// mfma_settle_short() before the product (dq_step places it before the
+// first dS chunk's products and between chunks); vector code reads the
+// result only after mfma_settle() or agpr_settle().  The CPU test
+// test_dq_hazards_cpu.py checks these distances on the built kernel.
 __device__ __forceinline__ void mfma_f16_agpr(f32x16& acc, const f16x8& a, const f16x8& b) {
   asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }

@@ -169,3 +169,32 @@ def test_window_f32(dev, orc):
     o, lse = orc.fwd(p, orc.keys(), *(host_bits(x) for x in (q, k, v)))
     assert max_abs(got["o"], o) <= TOL_F32
     assert max_abs(got["lse"], lse) <= TOL_F32
+
+
+@pytest.mark.parametrize("kv_ranges,local", [([(16, 80)], True), ([(0, 40), (96, 160)], False), ([], True)])
+def test_f32_share_calls(dev, orc, kv_ranges, local):
+    """fp32 forward of a share (a clean query range and three scattered
+    blocks, GQA 8/2, d = 128) over partial key sets: every row against the
+    oracle restricted to the call's keys (rows that see none: O = 0,
+    LSE = -inf)."""
+    from block_diffusion_lm_bdlm_amd import bdattn as B
+    L, M, hq, hkv, d = 192, 16, 8, 2, 128
+    blocks, clean_q = [1, 2, 9], [(40, 100)]
+    q, k, v, _ = doubled_inputs(31, 1, L, hq, hkv, d, dtype=torch.float32, device=dev)
+    pos = torch.tensor([L + b_ * M + i for b_ in blocks for i in range(M)], device=dev)
+    prob = B.problem(1, L, M, hq, hkv, d, B.BDATTN_F32)
+    sh = B.share(blocks, clean_q)
+    kvs = B.kv(kv_ranges, local)
+    R = 60 + len(blocks) * M
+    o = torch.full((1, R, hq, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((1, R, hq), float("nan"), dtype=torch.float32, device=dev)
+    qx, kx, vx = (t.index_select(1, pos).contiguous() for t in (q, k, v))
+    B.bdattn_fwd(prob, sh, kvs, q[:, 40:100], qx, k[:, :L], v[:, :L], kx, vx, o, B.BDATTN_F32, lse, None)
+    torch.cuda.synchronize()
+    p = orc.problem(1, L, M, hq, hkv, d)
+    rows = np.concatenate([np.arange(40, 100), pos.cpu().numpy()])
+    n = rows.size * hq
+    ro, rl = orc.fwd_rows(p, orc.keys(kv_ranges, local), *(host_bits(x) for x in (q, k, v)), np.zeros(n, np.int32),
+                          np.tile(np.arange(hq), rows.size), np.repeat(rows, hq))
+    assert max_abs(o.cpu().numpy().reshape(n, d), ro) <= TOL_F32
+    assert max_abs(lse.cpu().numpy().reshape(n), rl) <= TOL_F32
