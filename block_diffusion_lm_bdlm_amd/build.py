@@ -19,23 +19,18 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
 VOCAB_LIB = os.path.join(HERE, "libbdvocab.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["bdattn.cpp", "static_fwd.cpp", "fwd.hip", "fwd_f32.hip", "pack.hip", "bwd.hip", "dkdv.hip", "merge.hip"]
+SOURCES = ["bdattn.cpp", "static_fwd.cpp", "fwd.hip", "fwd_f32.hip", "pack.hip", "dq.hip", "dkdv.hip", "merge.hip"]
 VOCAB_SOURCES = ["bdvocab.cpp", "vocab_rows.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 VOCAB_LINK = ["-L", os.path.join(ROCM, "lib"), "-lhipblaslt", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
 # Per-file code generation options for the bf16 kernels: every matrix
-# product the compiler emits uses the VGPR form, so scores feed vector code
-# with no AGPR -> VGPR copies; the backward kernels keep their long-lived
-# accumulators in AGPRs through inline-assembly products.  The global->LDS
-# copies set M0 in inline assembly; these files make no other use of M0, so
-# the reserved-register warning is off.
+# product is a compiler builtin in the VGPR form, so scores feed vector code
+# with no AGPR -> VGPR copies and the compiler places every wait state
+# around the products.  The global->LDS copies set M0 in inline assembly;
+# these files make no other use of M0, so the reserved-register warning is
+# off.
 _MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]
-# The dQ kernel is scheduled with the compiler's iterative ILP strategy:
-# 113.4 against 118.9 ms at 64K on one box (the forward and dK/dV kernels
-# showed no gain from any strategy).  Its generated code keeps every read of
-# an inline-assembly product's result behind the hand-placed wait states.
-EXTRA = {"dkdv.hip": _MFMA_VGPR, "fwd.hip": _MFMA_VGPR,
-         "bwd.hip": _MFMA_VGPR + ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+EXTRA = {"dkdv.hip": _MFMA_VGPR, "fwd.hip": _MFMA_VGPR, "dq.hip": _MFMA_VGPR}
 ARCH = os.environ.get("BDATTN_ARCH", "gfx950")
 
 

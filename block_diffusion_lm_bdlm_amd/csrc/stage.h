@@ -138,61 +138,6 @@ __device__ __forceinline__ f16x8 tr_frag(const _Float16* step, const LaneOff<D>&
                                  6, 7);
 }
 
-// acc += A B with the accumulator held in AGPRs for the whole walk.  The
-// product is written as inline assembly so the accumulator stays in the
-// AGPRs while every other product (compiled in the VGPR form) feeds vector
-// code directly.  The compiler places no wait states around inline
-// assembly.  Operands loaded from LDS are covered by the waitcnt the
-// compiler emits for the asm's inputs; operands written by vector
-// instructions are not interlocked for the matrix core and need the fenced
-// mfma_settle_short() before the product (dq_step places it before the
-// first dS chunk's products and between chunks); vector code reads the
-// result only after mfma_settle() or agpr_settle().  The CPU test
-// test_dq_hazards_cpu.py checks these distances on the built kernel.
-__device__ __forceinline__ void mfma_f16_agpr(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// acc = A B (first) or acc += A B with B held in AGPRs and the result in
-// VGPRs, for operands that stay in registers for a whole walk.
-__device__ __forceinline__ f32x16 mfma_f16_bagpr0(const f16x8& a, const f16x8& b) {
-  f32x16 d;
-  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-  return d;
-}
-__device__ __forceinline__ void mfma_f16_bagpr(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
-// Pins a register value in AGPRs (no instruction).
-template <typename T>
-__device__ __forceinline__ void keep_in_agpr(T& x) {
-  asm volatile("" : "+a"(x));
-}
-// Wait states around inline-assembly products, which the compiler's own
-// wait-state placement cannot see.  Each is fenced by scheduling barriers
-// so that no instruction crosses it: the compiler could otherwise move a
-// vector read of a product's result (or a vector write of its operand)
-// past the wait, which nothing in the data flow forbids.
-// Between products whose results vector code reads next, or between vector
-// writes and products that read them (covers both).
-__device__ __forceinline__ void mfma_settle() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// Between vector writes and a product that reads them.
-__device__ __forceinline__ void mfma_settle_short() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 3");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// Before vector code may read an accumulator that a product just wrote
-// (more than a 32x32x16 product's 16 passes).
-__device__ __forceinline__ void agpr_settle() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Fragment reads kept in flight ahead of the products that consume them;
 // scheduling barriers pin this order (the compiler otherwise sinks each
 // read to its first use).  Measured at 2..10 on the 64K workload: 2-4 are
@@ -219,6 +164,50 @@ __device__ __forceinline__ void scores_2kb(const uint16_t* tile, int ql, const b
     }
     const int kb = f & 1, ks = f >> 1;
     acc[kb] = mfma_bf16(fr[f], row[ks], ks ? acc[kb] : f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// C^T block of 32 rows of a staged natural fp16 tile (starting at `block`)
+// times the lane's fp16 row held in registers: acc = block[0 .. 32][:] row^T,
+// kAhead fragment reads in flight.
+template <int D>
+__device__ __forceinline__ f32x16 scores_1kb_f16(const _Float16* block, int ql, const f16x8 (&row)[D / 16],
+                                                 const LaneOff<D>& o) {
+  constexpr int NF = D / 16;
+  const _Float16* tb = block + ql * D;
+  f16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + o.nat[f]);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) fr[f + kAhead] = ld16<f16x8>(tb + o.nat[f + kAhead]);
+    acc = mfma_f16(fr[f], row[f], acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
+// The same for a staged fp16 tile and fp16 rows.
+template <int D>
+__device__ __forceinline__ void scores_2kb_f16(const _Float16* tile, int ql, const f16x8 (&row)[D / 16],
+                                               const LaneOff<D>& o, f32x16 (&acc)[2]) {
+  constexpr int NF = 2 * (D / 16);
+  const _Float16* tb = tile + ql * D;
+  f16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) {
+      const int h = f + kAhead;
+      fr[h] = ld16<f16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
+    }
+    const int kb = f & 1, ks = f >> 1;
+    acc[kb] = mfma_f16(fr[f], row[ks], ks ? acc[kb] : f32x16{});
     __builtin_amdgcn_sched_barrier(0);
   }
 }
