@@ -63,7 +63,9 @@ def measured_traffic(kernel):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f).get(kernel)
-    if not rec or sources_sha(rec["sources"]) != rec["sha256"]:
+    if not rec or not all(os.path.exists(os.path.join(ROOT, r)) for r in rec["sources"]):
+        return None
+    if sources_sha(rec["sources"]) != rec["sha256"]:
         return None
     return int(rec["bytes_per_launch"])
 
