@@ -15,8 +15,8 @@ BDVOCAB_OK, BDVOCAB_EINVAL, BDVOCAB_ENOTSUP, BDVOCAB_EHIP, BDVOCAB_EWORKSPACE, B
 BDVOCAB_BF16, BDVOCAB_F32 = 0, 1
 BDVOCAB_WS_ROW_LIST, BDVOCAB_WS_HEAD_GRAD = 1, 2
 
-EXPORTS = ("bdvocab_workspace_bytes", "bdvocab_loss", "bdvocab_status_string", "bdvocab_profile_enable",
-           "bdvocab_profile_read")
+EXPORTS = ("bdvocab_workspace_bytes", "bdvocab_loss", "bdvocab_tune", "bdvocab_status_string",
+           "bdvocab_profile_enable", "bdvocab_profile_read")
 
 
 class Problem(C.Structure):
@@ -45,6 +45,8 @@ def lib():
     L.bdvocab_workspace_bytes.restype = C.c_size_t
     L.bdvocab_loss.argtypes = [P(Problem), vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, C.c_size_t, vp]
     L.bdvocab_loss.restype = C.c_int
+    L.bdvocab_tune.argtypes = [P(Problem), C.c_int, vp, i64, vp, i64, vp, C.c_size_t, vp]
+    L.bdvocab_tune.restype = C.c_int
     L.bdvocab_status_string.argtypes = [C.c_int]
     L.bdvocab_status_string.restype = C.c_char_p
     L.bdvocab_profile_enable.argtypes = [C.c_int]
@@ -92,6 +94,14 @@ def bdvocab_loss(prob, h, h_stride, w_head, rows, targets, weights, lse, loss, l
                               ws_bytes, _stream(stream)), "bdvocab_loss")
 
 
+def bdvocab_tune(prob, flags, h, h_stride, w_head, dh_stride, workspace, stream=None):
+    """Times the GEMM candidates for the shapes of matching bdvocab_loss calls
+    (set-up call: synchronises the stream)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bdvocab_tune(C.byref(prob), int(flags), _p(h), int(h_stride), _p(w_head), int(dh_stride),
+                              _p(workspace), ws_bytes, _stream(stream)), "bdvocab_tune")
+
+
 def bdvocab_profile_enable(enable=True):
     _check(lib().bdvocab_profile_enable(1 if enable else 0), "bdvocab_profile_enable")
 
@@ -121,6 +131,12 @@ class VocabLoss:
             raise BdvocabError(BDVOCAB_EINVAL, "bdvocab_workspace_bytes")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.row_list = row_list
+
+    def tune(self, h, w_head, dh_stride=0, stream=None):
+        """Times the GEMM candidates for this workspace's calls (dh_stride: the
+        calls' dh row stride, 0 when they pass no dh)."""
+        flags = (BDVOCAB_WS_ROW_LIST if self.row_list else 0) | (BDVOCAB_WS_HEAD_GRAD if self.head_grad else 0)
+        bdvocab_tune(self.prob, flags, h, h.stride(0), w_head, dh_stride, self.workspace, stream)
 
     def __call__(self, h, w_head, targets, weights=None, rows=None, dh=None, lse=None, loss=None, loss_sum=None,
                  dw=None, stream=None):

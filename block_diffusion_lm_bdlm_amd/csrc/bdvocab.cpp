@@ -21,18 +21,15 @@
 // into the workspace): both products then read their two operands along
 // the contraction, the layout the library runs fastest (measured: the
 // gradient GEMM on W itself, not transposed, was 25-30% slower).
-// Algorithm choice: on the first use of a shape, the library's top
-// candidates are timed on the call's stream (which synchronises that first
-// call) and the fastest is kept for the process; BDVOCAB_TUNE=0 in the
-// environment keeps the library's first candidate instead.  The head GEMM
-// accumulates into the caller's dW, so it is never timed: it takes the
-// library's first candidate.
+// Algorithm choice: bdvocab_tune times the library's top candidates for
+// every GEMM shape a loss call of the same arguments will run (the head GEMM
+// on a scratch output, since its runs accumulate) and keeps the fastest per
+// shape for the process.  bdvocab_loss itself never times or synchronises:
+// a shape nobody tuned takes the library's first candidate.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -176,8 +173,12 @@ struct GemmDescs {
 
 // D (m x n, column-major, leading dimension ldd, type dt) = op(A) op(B)
 // (+ D when accumulate), A and B bf16.
+// tune: time the candidates on `s` (synchronising it), keep the fastest
+// for the shape and run nothing else; D is scratch then.  Otherwise run with
+// the kept algorithm, or the library's first candidate (kept from then on).
 int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, const void* B,
-         int64_t ldb, void* D, hipDataType dt, int64_t ldd, void* ws, hipStream_t s, bool accumulate = false) {
+         int64_t ldb, void* D, hipDataType dt, int64_t ldd, void* ws, hipStream_t s, bool accumulate = false,
+         bool tune = false) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BDVOCAB_EHIP;
   hipblasLtHandle_t h;
@@ -208,7 +209,7 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
   {
     std::lock_guard<std::mutex> lk(g_blas.mu);
     auto it = g_blas.algos.find(key);
-    if (it != g_blas.algos.end()) {
+    if (it != g_blas.algos.end() && !tune) {
       best = it->second;
     } else {
       hipblasLtMatmulPreference_t pref = nullptr;
@@ -222,8 +223,6 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
       hipblasLtMatmulPreferenceDestroy(pref);
       if (st != HIPBLAS_STATUS_SUCCESS || found < 1) return BDVOCAB_EBLAS;
       int pick = -1;
-      const char* env = std::getenv("BDVOCAB_TUNE");
-      const bool tune = found > 1 && !accumulate && !(env && std::strcmp(env, "0") == 0);
       if (tune) {
         hipEvent_t e0 = nullptr, e1 = nullptr;
         if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return BDVOCAB_EHIP;
@@ -231,12 +230,13 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
         const float one = 1.f, zero = 0.f;
         for (int i = 0; i < found; ++i) {
           if (cand[i].state != HIPBLAS_STATUS_SUCCESS || cand[i].workspaceSize > kBlasWs) continue;
-          // one untimed run, then two timed ones
-          bool ok = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, &zero, D, g.d, D, g.d, &cand[i].algo, ws,
+          // one untimed run, then two timed ones (accumulating runs add into the scratch D)
+          const float* beta = accumulate ? &one : &zero;
+          bool ok = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, beta, D, g.d, D, g.d, &cand[i].algo, ws,
                                     kBlasWs, s) == HIPBLAS_STATUS_SUCCESS;
           ok = ok && hipEventRecord(e0, s) == hipSuccess;
           for (int r = 0; ok && r < 2; ++r)
-            ok = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, &zero, D, g.d, D, g.d, &cand[i].algo, ws, kBlasWs,
+            ok = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, beta, D, g.d, D, g.d, &cand[i].algo, ws, kBlasWs,
                                  s) == HIPBLAS_STATUS_SUCCESS;
           ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
           float ms = 0.f;
@@ -257,6 +257,7 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
       g_blas.algos[key] = best;
     }
   }
+  if (tune) return BDVOCAB_OK;
   const float one = 1.f, zero = 0.f;
   const hipblasStatus_t st = hipblasLtMatmul(h, g.op, &one, A, g.a, B, g.b, accumulate ? &one : &zero, D, g.d, D,
                                              g.d, &best.algo, ws, kBlasWs, s);
@@ -360,6 +361,59 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
   }
   if (loss_sum) return timed(K_SUM, s, [&] { return hip_rc(launch_loss_sum(loss, R, loss_sum, s)); });
   return BDVOCAB_OK;
+}
+
+int bdvocab_tune(const bdvocab_problem* problem, int flags, const void* h, int64_t h_stride, const void* w_head,
+                 int64_t dh_stride, void* workspace, size_t ws_bytes, void* hip_stream) {
+  const int pc = check_problem(problem);
+  if (pc != BDVOCAB_OK) return pc;
+  if (flags & ~(BDVOCAB_WS_ROW_LIST | BDVOCAB_WS_HEAD_GRAD)) return BDVOCAB_EINVAL;
+  const bdvocab_problem& p = *problem;
+  const int64_t R = p.n_rows, d = p.hidden;
+  if (R == 0) return BDVOCAB_OK;
+  const bool rows = (flags & BDVOCAB_WS_ROW_LIST) != 0, head = (flags & BDVOCAB_WS_HEAD_GRAD) != 0;
+  const int es = p.dh_dtype == BDVOCAB_F32 ? 4 : 2;
+  if (!h || !w_head || h_stride < d || h_stride % 8 != 0 || !aligned16(h) || !aligned16(w_head))
+    return BDVOCAB_EINVAL;
+  if (dh_stride < 0 || (dh_stride > 0 && (dh_stride < d || (dh_stride * es) % 16 != 0))) return BDVOCAB_EINVAL;
+  const Layout L = layout(p, rows, head);
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0 || ws_bytes < L.total)
+    return BDVOCAB_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* S = reinterpret_cast<float*>(ws + L.s_off);
+  void* blas_ws = ws + L.blas_off;
+  const hipDataType dt = p.dh_dtype == BDVOCAB_F32 ? HIP_R_32F : HIP_R_16BF;
+  // scratch outputs of the GEMMs whose real outputs are the caller's
+  const int64_t nmax = L.chunk;
+  const size_t dh_scratch = (dh_stride > 0 && !rows) ? (size_t)nmax * dh_stride * es : 0;
+  const size_t dw_scratch = head ? (size_t)p.vocab * d * 4 : 0;
+  void* scratch = nullptr;
+  if (dh_scratch + dw_scratch > 0 && hipMalloc(&scratch, round_up(dh_scratch, kAlign) + dw_scratch) != hipSuccess)
+    return BDVOCAB_EHIP;
+  uint8_t* sc = static_cast<uint8_t*>(scratch);
+  float* dw_sc = reinterpret_cast<float*>(sc + round_up(dh_scratch, kAlign));
+  int rc = BDVOCAB_OK;
+  // the chunk sizes a loss call runs: full chunks and the last, shorter one
+  int64_t sizes[2] = {std::min<int64_t>(L.chunk, R), R % L.chunk};
+  const int nsizes = (R > L.chunk && sizes[1] > 0) ? 2 : 1;
+  for (int i = 0; i < nsizes && rc == BDVOCAB_OK; ++i) {
+    const int64_t n = sizes[i];
+    const void* Hb = rows ? static_cast<const void*>(ws + L.hc_off) : h;
+    const int64_t ldh = rows ? d : h_stride;
+    rc = gemm(true, false, p.vocab, n, d, w_head, d, Hb, ldh, S, HIP_R_32F, L.ld, blas_ws, s, false, true);
+    if (rc == BDVOCAB_OK && dh_stride > 0) {
+      void* D = rows ? static_cast<void*>(ws + L.dhc_off) : scratch;
+      const int64_t ldd = rows ? d : dh_stride;
+      rc = gemm(true, false, d, n, p.vocab, ws + L.wt_off, L.ld, S, 2 * L.ld, D, dt, ldd, blas_ws, s, false, true);
+    }
+    if (rc == BDVOCAB_OK && head)
+      rc = gemm(true, false, d, p.vocab, n, ws + L.ht_off, L.ldc, ws + L.gt_off, L.ldc, dw_sc, HIP_R_32F, d,
+                blas_ws, s, true, true);
+  }
+  if (hipStreamSynchronize(s) != hipSuccess && rc == BDVOCAB_OK) rc = BDVOCAB_EHIP;
+  if (scratch && hipFree(scratch) != hipSuccess && rc == BDVOCAB_OK) rc = BDVOCAB_EHIP;
+  return rc;
 }
 
 const char* bdvocab_status_string(int status) {

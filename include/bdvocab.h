@@ -33,16 +33,19 @@
  * a third, when dW is requested, adds the chunk's G^T H to dW (from
  * transposed copies of G and H, so that both operands run along the
  * contraction).
- * Device memory for logits is C * V * 4 bytes, never R * V.  The first call
- * of a shape times the GEMM library's candidate algorithms on the call's
- * stream (synchronising that call) and keeps the fastest; BDVOCAB_TUNE=0
- * in the environment keeps the library's first candidate.
+ * Device memory for logits is C * V * 4 bytes, never R * V.  bdvocab_tune
+ * (a set-up call) times the GEMM library's candidate algorithms for the
+ * shapes of a loss call and keeps the fastest per shape; bdvocab_loss never
+ * times or synchronises, and a shape nobody tuned takes the library's first
+ * candidate.
  *
  * Conventions.
  *   - Device buffers are caller-owned and scratch comes from `workspace`
- *     (size from bdvocab_workspace_bytes).  This library allocates no
+ *     (size from bdvocab_workspace_bytes).  bdvocab_loss allocates no
  *     device memory itself; the GEMM library (hipBLASLt) creates its handle
- *     once per device on the first call and may allocate inside it.
+ *     once per device on the first call of either entry point and may
+ *     allocate inside it, so a caller that captures bdvocab_loss into a
+ *     graph calls bdvocab_tune (or bdvocab_loss) once before.
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL =
  *     the null stream); buffers must stay valid until it completes.  Calls
  *     sharing a workspace must not overlap.
@@ -108,9 +111,7 @@ size_t bdvocab_workspace_bytes(const bdvocab_problem* problem, int flags);
  *            >= d.
  *   dw       fp32 [V, d] row-major, contiguous, device, or NULL.  The call
  *            ADDS its gradient (dw += sum_r g_r^T h_r), so the caller
- *            clears it before the first call of a step.  Its GEMM takes the
- *            library's first algorithm (never the timing search, whose runs
- *            would accumulate).
+ *            clears it before the first call of a step.
  *   workspace / ws_bytes: at least bdvocab_workspace_bytes(problem,
  *            (rows ? BDVOCAB_WS_ROW_LIST : 0) | (dw ? BDVOCAB_WS_HEAD_GRAD
  *            : 0)); the contents need not be initialised.
@@ -119,6 +120,27 @@ int bdvocab_loss(const bdvocab_problem* problem, const void* h, int64_t h_stride
                  const void* w_head, const int32_t* rows, const int32_t* targets,
                  const float* weights, float* lse, float* loss, float* loss_sum,
                  void* dh, int64_t dh_stride, float* dw, void* workspace, size_t ws_bytes,
+                 void* hip_stream);
+
+/* Set-up call: times the GEMM library's candidate algorithms for every GEMM
+ * shape a bdvocab_loss call with the same problem and the same kind of
+ * arguments runs (full chunks and the last, shorter chunk; the head
+ * gradient GEMM on a scratch output, since its runs accumulate) and keeps
+ * the fastest per shape for the process.
+ *   flags     BDVOCAB_WS_ROW_LIST when the loss calls pass a row list,
+ *             BDVOCAB_WS_HEAD_GRAD when they pass dw.
+ *   h, h_stride, w_head: as in bdvocab_loss (only their addresses, strides
+ *             and the shapes are used; the values are not read for
+ *             results).
+ *   dh_stride the loss calls' dh_stride, or 0 when they pass no dh.
+ *   workspace / ws_bytes: as in bdvocab_loss for these flags; its contents
+ *             are overwritten.
+ * Unlike bdvocab_loss it synchronises `hip_stream` and allocates (and
+ * frees) scratch device memory for the outputs it must not write: the dh
+ * rows (without a row list) and a V x d fp32 head gradient.  Calling it is
+ * optional; calling it again re-times.  R = 0 does nothing. */
+int bdvocab_tune(const bdvocab_problem* problem, int flags, const void* h, int64_t h_stride,
+                 const void* w_head, int64_t dh_stride, void* workspace, size_t ws_bytes,
                  void* hip_stream);
 
 /* Static text for a bdvocab_status value. */

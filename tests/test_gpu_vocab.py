@@ -39,7 +39,7 @@ def _host(t):
 
 
 def _run(dev, seed, T, R, V, d, chunk, row_list, dh_dtype, weighted=True, ignored=(), head_std=None, head_grad=True,
-         dw_repeat=1, with_dh=True):
+         dw_repeat=1, with_dh=True, tuned=False):
     from block_diffusion_lm_bdlm_amd import bdvocab as BV
     from block_diffusion_lm_bdlm_amd import synth
     print(f"\n[vocab] seed={seed} T={T} R={R} V={V} d={d} chunk={chunk} rows={row_list} dh={dh_dtype}", flush=True)
@@ -61,6 +61,8 @@ def _run(dev, seed, T, R, V, d, chunk, row_list, dh_dtype, weighted=True, ignore
     loss_sum = torch.empty(1, dtype=torch.float32, device=dev)
     rows_dev = None if rows is None else rows.to(dev)
     dw = torch.zeros((V, d), dtype=torch.float32, device=dev) if head_grad else None
+    if tuned:  # set-up call: must not touch dh, dw or the loss outputs
+        vl.tune(h, W, dh_stride=dh.stride(0) if with_dh else 0)
     for _ in range(dw_repeat):
         loss, _, _, _ = vl(h, W, y, weights=wt, rows=rows_dev, dh=dh if with_dh else None, lse=lse,
                            loss_sum=loss_sum, dw=dw)
@@ -114,11 +116,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("tuned", [False, True], ids=["untuned", "tuned"])
 @pytest.mark.parametrize("case", CASES, ids=[f"R{c[2]}_V{c[3]}_d{c[4]}_C{c[5]}_{'rows' if c[6] else 'dense'}"
                                              for c in CASES])
-def test_vocab_parity(dev, case):
+def test_vocab_parity(dev, case, tuned):
+    """With and without bdvocab_tune first (the GEMMs then run the timed
+    algorithms of every shape, the head gradient GEMM included)."""
     seed, T, R, V, d, chunk, row_list, dt = case
-    _check(_run(dev, seed, T, R, V, d, chunk, row_list, dt))
+    _check(_run(dev, seed, T, R, V, d, chunk, row_list, dt, tuned=tuned))
 
 
 def test_vocab_ignored_targets_and_unit_weights(dev):

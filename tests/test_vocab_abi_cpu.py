@@ -20,7 +20,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 5
+    assert len(names) == 6
     lib = C.CDLL(BV.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -104,3 +104,29 @@ def test_invalid_arguments_rejected_on_host():
     assert _status(BV.problem(0, 100, 64), None, 64, None, None, None, None, None, None, None, None, 0, None, None) \
         == BV.BDVOCAB_OK
     assert BV.bdvocab_status_string(BV.BDVOCAB_EBLAS).startswith("GEMM library")
+
+
+def _tune_status(*a):
+    try:
+        BV.bdvocab_tune(*a, stream=0)
+    except BV.BdvocabError as e:
+        return e.status
+    return BV.BDVOCAB_OK
+
+
+def test_tune_arguments_rejected_on_host():
+    """bdvocab_tune checks its arguments like bdvocab_loss, before any HIP
+    call; R = 0 has nothing to tune."""
+    p = BV.problem(4, 100, 64)
+    ws_need = BV.bdvocab_workspace_bytes(p, False)
+    h, w, ws = _Fake(4096), _Fake(8192), _Fake(1 << 20, ws_need)
+    assert _tune_status(BV.problem(1, 10, 12), 0, h, 64, w, 0, ws) == BV.BDVOCAB_ENOTSUP
+    assert _tune_status(p, 4, h, 64, w, 0, ws) == BV.BDVOCAB_EINVAL                 # unknown flag bit
+    assert _tune_status(p, 0, None, 64, w, 0, ws) == BV.BDVOCAB_EINVAL              # no h
+    assert _tune_status(p, 0, h, 32, w, 0, ws) == BV.BDVOCAB_EINVAL                 # stride < d
+    assert _tune_status(p, 0, h, 64, None, 0, ws) == BV.BDVOCAB_EINVAL              # no head
+    assert _tune_status(p, 0, h, 64, w, 60, ws) == BV.BDVOCAB_EINVAL                # dh stride < d
+    assert _tune_status(p, 0, h, 64, w, -1, ws) == BV.BDVOCAB_EINVAL
+    assert _tune_status(p, 0, h, 64, w, 0, _Fake(1 << 20, ws_need - 1)) == BV.BDVOCAB_EWORKSPACE
+    assert _tune_status(p, BV.BDVOCAB_WS_HEAD_GRAD, h, 64, w, 0, ws) == BV.BDVOCAB_EWORKSPACE
+    assert _tune_status(BV.problem(0, 100, 64), 0, None, 64, None, 0, None) == BV.BDVOCAB_OK
