@@ -11,8 +11,8 @@
 // waves per SIMD: one wave's exponentials and dS run under the other's
 // matrix products).  A wave holds its rows' Q and dO as B operands and its
 // dQ^T accumulators, and per key tile of 64 keys computes
-//   S^T = K Q^T,  P^T = exp2(S^T c2 - LSE2) (masked),  dP^T = V dO^T,
-//   dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T,
+//   S^T = K Q^T and dP^T = V dO^T (interleaved),
+//   P^T = exp2(S^T c2 - LSE2) (masked),  dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T,
 // with K and V (fp16 rows) staged double buffered in LDS (global_load_lds)
 // and K^T fragments read across the rows of the staged K tile.  All products
 // are compiler builtins, so the compiler places every wait state.  (One
@@ -111,9 +111,11 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
       if (!full) compact_range(P.k[ri], rb, clean, &vlo, &vhi);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T = K Q^T; the other wave of the SIMD runs its vector work meanwhile
+        // S^T = K Q^T and dP^T = V dO^T, as two interleaved chains; the other
+        // wave of the SIMD runs its vector work meanwhile
+        f32x16 sacc, pacc;
         __builtin_amdgcn_s_setprio(2);
-        f32x16 sacc = scores_1kb_f16<D>(kt + kb * 32 * D, ql, qreg, o);
+        scores_1kb_pair_f16<D>(kt + kb * 32 * D, qreg, sm.v[buf] + kb * 32 * D, doreg, ql, o, sacc, pacc);
         __builtin_amdgcn_s_setprio(0);
         if (!full) {
 #pragma unroll
@@ -126,10 +128,6 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           pf[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -lse2));
-        // dP^T = V dO^T
-        __builtin_amdgcn_s_setprio(2);
-        const f32x16 pacc = scores_1kb_f16<D>(sm.v[buf] + kb * 32 * D, ql, doreg, o);
-        __builtin_amdgcn_s_setprio(0);
         // dS^T = P^T (dP^T - D), with dP - D rounded to fp16 before the product
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {

@@ -168,46 +168,37 @@ __device__ __forceinline__ void scores_2kb(const uint16_t* tile, int ql, const b
   }
 }
 
-// C^T block of 32 rows of a staged natural fp16 tile (starting at `block`)
-// times the lane's fp16 row held in registers: acc = block[0 .. 32][:] row^T,
-// kAhead fragment reads in flight.
+// Two C^T blocks of 32 rows of staged natural fp16 tiles (starting at
+// block_a, block_b) times the lane's fp16 rows held in registers, their
+// products interleaved: acc_a = block_a row_a^T, acc_b = block_b row_b^T.
+// Two independent accumulation chains
+// let each product issue while the other chain's last result is still in
+// flight (measured on the dQ kernel: -1.6% against one chain after the
+// other); two reads per chain stay in flight ahead of the products.
 template <int D>
-__device__ __forceinline__ f32x16 scores_1kb_f16(const _Float16* block, int ql, const f16x8 (&row)[D / 16],
-                                                 const LaneOff<D>& o) {
-  constexpr int NF = D / 16;
-  const _Float16* tb = block + ql * D;
-  f16x8 fr[NF];
+__device__ __forceinline__ void scores_1kb_pair_f16(const _Float16* block_a, const f16x8 (&row_a)[D / 16],
+                                                    const _Float16* block_b, const f16x8 (&row_b)[D / 16], int ql,
+                                                    const LaneOff<D>& o, f32x16& acc_a, f32x16& acc_b) {
+  constexpr int NF = D / 16, AH = 2;
+  const _Float16* ta = block_a + ql * D;
+  const _Float16* tb = block_b + ql * D;
+  f16x8 fa[NF], fb[NF];
 #pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + o.nat[f]);
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 acc = f32x16{};
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    if (f + kAhead < NF) fr[f + kAhead] = ld16<f16x8>(tb + o.nat[f + kAhead]);
-    acc = mfma_f16(fr[f], row[f], acc);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int f = 0; f < AH; ++f) {
+    fa[f] = ld16<f16x8>(ta + o.nat[f]);
+    fb[f] = ld16<f16x8>(tb + o.nat[f]);
   }
-  return acc;
-}
-
-// The same for a staged fp16 tile and fp16 rows.
-template <int D>
-__device__ __forceinline__ void scores_2kb_f16(const _Float16* tile, int ql, const f16x8 (&row)[D / 16],
-                                               const LaneOff<D>& o, f32x16 (&acc)[2]) {
-  constexpr int NF = 2 * (D / 16);
-  const _Float16* tb = tile + ql * D;
-  f16x8 fr[NF];
-#pragma unroll
-  for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(tb + (f & 1) * 32 * D + o.nat[f >> 1]);
   __builtin_amdgcn_sched_barrier(0);
+  acc_a = f32x16{};
+  acc_b = f32x16{};
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    if (f + kAhead < NF) {
-      const int h = f + kAhead;
-      fr[h] = ld16<f16x8>(tb + (h & 1) * 32 * D + o.nat[h >> 1]);
+    if (f + AH < NF) {
+      fa[f + AH] = ld16<f16x8>(ta + o.nat[f + AH]);
+      fb[f + AH] = ld16<f16x8>(tb + o.nat[f + AH]);
     }
-    const int kb = f & 1, ks = f >> 1;
-    acc[kb] = mfma_f16(fr[f], row[ks], ks ? acc[kb] : f32x16{});
+    acc_a = mfma_f16(fa[f], row_a[f], acc_a);
+    acc_b = mfma_f16(fb[f], row_b[f], acc_b);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
