@@ -145,29 +145,31 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float mc = m_use * c2;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run * c2 - mc) : 1.f;
-      f16x8 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pf[kb][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -mc));
-      // the normaliser sums the fp16 probabilities the O product uses, two
-      // per instruction (fp32 accumulation)
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const f16x2 pp = {pf[kb][hf][e], pf[kb][hf][e + 1]};
-            lsum = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, lsum, false);
-          }
-      l_run = l_run * alpha + lsum;
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       }
       m_run = m_new;
+      // P of 16-key step s (8 values per lane, kb = s / 2) and its share of
+      // the normaliser, which sums the fp16 probabilities the O product uses,
+      // two per instruction (fp32 accumulation).  Step s + 1's exponentials
+      // are issued after step s's O products, so they run while those
+      // products occupy the matrix core (-1% at 64K, -2% at 8K against all
+      // exponentials first).
+      f16x8 pf[2][2];
+      float lsum = 0.f;
+      auto p_step = [&](int s) {
+        const int kb = s >> 1, hf = s & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[kb][hf][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][hf * 8 + e], c2, -mc));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const f16x2 pp = {pf[kb][hf][e], pf[kb][hf][e + 1]};
+          lsum = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+        }
+      };
+      p_step(0);
       // O^T += V^T P^T
       __builtin_amdgcn_s_setprio(2);
       {
@@ -184,8 +186,13 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
           const int s = f / NDB, db = f % NDB;
           oacc[db] = mfma_f16(fr[f], pf[s >> 1][s & 1], oacc[db]);
           __builtin_amdgcn_sched_barrier(0);
+          if (db == NDB - 1 && s + 1 < kBK / 16) {
+            p_step(s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
+      l_run = l_run * alpha + lsum;
       __builtin_amdgcn_s_setprio(0);
       wait_copies();
       __syncthreads();  // the next tile's copies have landed; this tile's reads are done
