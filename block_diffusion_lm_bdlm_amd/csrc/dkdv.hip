@@ -329,9 +329,11 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
         s_phase_a<D, true>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
       else
         s_phase_a<D, false>(sm, B, kw, lane, ql, hh, mysrc, c2, kvreg, o, pf);
+      __builtin_amdgcn_sched_barrier(0);  // the P writes stay ahead of the reads below
       f16x8 fr[kRcFrags<D>];
       rows_contract_head<D>(sm.dO[B], o, fr);
-      barrier_lds();  // P visible to the P-waves
+      // P visible to the P-waves; the 2 kAhead transposed reads just issued stay in flight
+      barrier_lds_behind<2 * kAhead>();
       rows_contract<D>(sm.dO[B], o, pf, acc, fr);  // dV^T += dO^T P
     } else {
       f32x16 pacc[kRB][kKB];
@@ -339,7 +341,7 @@ __device__ __forceinline__ void dkdv_walk(const Plan& P, const DkdvArgs& A, Dkdv
       p_phase_a<D>(sm, B, ql, hh, kvreg, o, pacc, dcs);
       f16x8 fr[kRcFrags<D>];
       rows_contract_head<D>(sm.q[B], o, fr);
-      barrier_lds();  // P from the S-waves
+      barrier_reads_in_flight();  // P from the S-waves
       f16x8 dsf[kRB][kKB][2];
       p_phase_ds<D>(sm, kw, lane, dcs, pacc, dsf);
       rows_contract<D>(sm.q[B], o, dsf, acc, fr);  // dK^T += Q^T dS

@@ -49,6 +49,25 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// Barrier that publishes this wave's LDS writes while the N LDS reads it
+// issued after them stay in flight: a wave's LDS operations complete in
+// order, so lgkmcnt(N) covers every write issued before those reads.  The
+// caller pins the order (no scalar memory operation may be outstanding,
+// those complete out of order).
+template <int N>
+__device__ __forceinline__ void barrier_lds_behind() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt holds 0..15");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f | (N << 8));  // lgkmcnt(N)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Barrier for a wave that publishes no LDS writes: its reads stay in flight.
+__device__ __forceinline__ void barrier_reads_in_flight() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 
 // Staged tiles are unpadded; 16-byte chunk c of row r sits at chunk
