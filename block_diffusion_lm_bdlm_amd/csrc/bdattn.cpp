@@ -161,10 +161,11 @@ struct Carve {
   }
 };
 
-// Every bf16 workspace starts with a 256-byte header whose first int32 is
+// Every bf16 workspace starts with a 4 KB header whose first int32 is
 // the call's range flag (cleared by the call, set by the packing kernels
-// when a value converted to fp16 lies outside the half range).
-constexpr size_t kHeaderBytes = 256;
+// when a value converted to fp16 lies outside the half range), followed by
+// the kernels' work-queue heads (kernels.h).
+constexpr size_t kHeaderBytes = 4 * kHeaderWords;
 
 struct FwdWs {
   int32_t* flag;
@@ -425,6 +426,7 @@ int fwd_impl(const bdattn_problem* problem, const bdattn_share* share, const bda
   a.o_hs = o.head_stride;
   a.o_f32 = o_dtype == BDATTN_F32;
   a.lse = lse;
+  a.queue = ws.flag + kQueueFwd;
   return hip_status(timed(K_FWD, s, [&] { return launch_fwd_bf16(P, a, s); }));
 }
 
@@ -527,10 +529,10 @@ int bdattn_bwd(const bdattn_problem* problem, const bdattn_share* share, const b
   e = timed(K_PACK_K, s, [&] { return launch_pack_k(P, pk, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
   DkdvArgs ka{ws.qh, ws.doh, ws.lse2, ws.dc, ws.vis, ws.kh, ws.vh,
-              dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc, overwrite ? 1 : 0};
+              dk_clean_acc, dv_clean_acc, dk_corr_acc, dv_corr_acc, overwrite ? 1 : 0, ws.flag + kQueueDkdv};
   e = timed(K_DKDV, s, [&] { return launch_dkdv(P, ka, s); });
   if (e != hipSuccess) return BDATTN_EHIP;
-  DqArgs qa{ws.qh, ws.doh, ws.lse2, ws.dc, ws.kh, ws.vh, dq_acc, overwrite ? 1 : 0};
+  DqArgs qa{ws.qh, ws.doh, ws.lse2, ws.dc, ws.kh, ws.vh, dq_acc, overwrite ? 1 : 0, ws.flag + kQueueDq};
   return hip_status(timed(K_DQ, s, [&] { return launch_dq(P, qa, s); }));
 }
 

@@ -471,7 +471,17 @@ __device__ void dkdv_tile(const Plan& P, const DkdvArgs& A, DkdvSmem<D>& sm, int
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const Plan P, const DkdvArgs A) {
   __shared__ DkdvSmem<D> sm;
-  const WgK wg = decode_wg_k(P, blockIdx.x);
+  __shared__ int64_t item;
+  // one work item from the XCD queues (plan.h); a spare workgroup that
+  // finds every queue empty ends here
+  if (threadIdx.x == 0) {
+    int scan = 0;
+    item = next_item(A.queue, kQueueStride, P.nwg_k, (int)(blockIdx.x % kXCD), &scan);
+  }
+  __syncthreads();
+  const int64_t l = item;
+  if (l < 0) return;
+  const WgK wg = decode_item_k(P, l);
   dkdv_tile<D>(P, A, sm, wg.b, wg.g, wg.tile_a);
   if (wg.tile_b >= 0) {
     __syncthreads();
@@ -484,9 +494,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const Plan P, const D
 hipError_t launch_dkdv(const Plan& P, const DkdvArgs& a, hipStream_t s) {
   if (P.nwg_k == 0) return hipSuccess;
   if (P.d == 128)
-    hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)P.nwg_k), dim3(kThreads), 0, s, P, a);
+    hipLaunchKernelGGL(dkdv_kernel<128>, dim3(queue_grid(P.nwg_k)), dim3(kThreads), 0, s, P, a);
   else
-    hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)P.nwg_k), dim3(kThreads), 0, s, P, a);
+    hipLaunchKernelGGL(dkdv_kernel<64>, dim3(queue_grid(P.nwg_k)), dim3(kThreads), 0, s, P, a);
   return hipGetLastError();
 }
 

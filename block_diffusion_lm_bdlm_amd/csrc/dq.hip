@@ -184,7 +184,17 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
 template <int D>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void dq_kernel(const Plan P, const DqArgs A) {
   __shared__ DqSmem<D> sm;
-  const WgQ wg = decode_wg_q(P, blockIdx.x);
+  __shared__ int64_t item;
+  // one work item from the XCD queues (plan.h); a spare workgroup that
+  // finds every queue empty ends here
+  if (threadIdx.x == 0) {
+    int scan = 0;
+    item = next_item(A.queue, kQueueStride, P.nwg_q, (int)(blockIdx.x % kXCD), &scan);
+  }
+  __syncthreads();
+  const int64_t l = item;
+  if (l < 0) return;
+  const WgQ wg = decode_item_q(P, l);
   dq_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);
   if (wg.tile_b >= 0) {
     __syncthreads();
@@ -197,9 +207,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void dq_kernel(const Plan P, cons
 hipError_t launch_dq(const Plan& P, const DqArgs& a, hipStream_t s) {
   if (P.nwg_q == 0) return hipSuccess;
   if (P.d == 128)
-    hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)P.nwg_q), dim3(64 * kDqWaves), 0, s, P, a);
+    hipLaunchKernelGGL(dq_kernel<128>, dim3(queue_grid(P.nwg_q)), dim3(64 * kDqWaves), 0, s, P, a);
   else
-    hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)P.nwg_q), dim3(64 * kDqWaves), 0, s, P, a);
+    hipLaunchKernelGGL(dq_kernel<64>, dim3(queue_grid(P.nwg_q)), dim3(64 * kDqWaves), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -243,7 +243,17 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const Plan P, const FwdArgs A) {
   __shared__ FwdSmem<D> sm;
-  const WgQ wg = decode_wg_q(P, blockIdx.x);
+  __shared__ int64_t item;
+  // one work item from the XCD queues (plan.h); a spare workgroup that
+  // finds every queue empty ends here
+  if (threadIdx.x == 0) {
+    int scan = 0;
+    item = next_item(A.queue, kQueueStride, P.nwg_q, (int)(blockIdx.x % kXCD), &scan);
+  }
+  __syncthreads();
+  const int64_t l = item;
+  if (l < 0) return;
+  const WgQ wg = decode_item_q(P, l);
   fwd_tile<D>(P, A, sm, wg.b, wg.h, wg.g, wg.tile_a);
   if (wg.tile_b >= 0) {
     __syncthreads();
@@ -256,9 +266,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const Plan P, const Fw
 hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s) {
   if (P.nwg_q == 0) return hipSuccess;
   if (P.d == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(queue_grid(P.nwg_q)), dim3(256), 0, s, P, a);
   else
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)P.nwg_q), dim3(256), 0, s, P, a);
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(queue_grid(P.nwg_q)), dim3(256), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -8,6 +8,15 @@
 
 namespace bd {
 
+// The header of every bf16 workspace (kHeaderWords int32): word 0 is the
+// call's range flag; words kQueueFwd, kQueueDq and kQueueDkdv start the
+// eight per-XCD work-queue heads of those kernels (plan.h), kQueueStride
+// words apart so each head has a 128-byte line of its own (claims on one
+// queue do not contend with the others).  The clear kernel zeroes the flag
+// and the heads at the start of each call.
+constexpr int kQueueStride = 32;
+constexpr int kQueueFwd = 256, kQueueDq = 512, kQueueDkdv = 768, kHeaderWords = 1024;
+
 struct TensorArg {
   const void* p;
   int64_t bs, rs, hs;  // strides in elements; head dim contiguous
@@ -55,6 +64,7 @@ struct FwdArgs {
   int64_t o_bs, o_rs, o_hs;
   int32_t o_f32;
   float* lse;  // [batch][R][hq]
+  int32_t* queue;  // per-XCD work-queue heads, zero at launch
 };
 
 struct FwdF32Args {
@@ -73,6 +83,7 @@ struct DqArgs {
   const _Float16* vh;
   float* dq;  // [batch][R][hq][d], += (= when overwrite)
   int32_t overwrite;
+  int32_t* queue;  // per-XCD work-queue heads, zero at launch
 };
 
 struct DkdvArgs {
@@ -88,6 +99,7 @@ struct DkdvArgs {
   float* dk_corr;   // [batch][n_corr_rows][hkv][d], += (= when overwrite)
   float* dv_corr;
   int32_t overwrite;
+  int32_t* queue;  // per-XCD work-queue heads, zero at launch
 };
 
 struct MergeArgs {
@@ -100,7 +112,7 @@ struct MergeArgs {
   uint16_t* o_bf16;
 };
 
-hipError_t launch_flag_clear(int32_t* flag, hipStream_t s);
+hipError_t launch_flag_clear(int32_t* header, hipStream_t s);  // zeroes the workspace header's first kHeaderWords
 hipError_t launch_pack_k(const Plan& P, const PackKArgs& a, hipStream_t s);
 hipError_t launch_pack_q(const Plan& P, const PackQArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const Plan& P, const FwdArgs& a, hipStream_t s);

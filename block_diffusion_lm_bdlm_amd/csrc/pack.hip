@@ -233,14 +233,20 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const Plan P, const PackQAr
   }
 }
 
-__global__ void flag_clear_kernel(int32_t* flag) {
-  if (threadIdx.x == 0) *reinterpret_cast<volatile int32_t*>(flag) = 0;
+// Zeroes the range flag and the work-queue heads of a workspace header.
+__global__ void flag_clear_kernel(int32_t* header) {
+  const int t = threadIdx.x;
+  volatile int32_t* h = header;
+  if (t == 0) h[0] = 0;
+  if (t < 3 * kXCD) h[kQueueFwd + (t / kXCD) * (kQueueDq - kQueueFwd) + (t % kXCD) * kQueueStride] = 0;
 }
 
 }  // namespace
 
-hipError_t launch_flag_clear(int32_t* flag, hipStream_t s) {
-  hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+hipError_t launch_flag_clear(int32_t* header, hipStream_t s) {
+  static_assert(kQueueDq - kQueueFwd == kQueueDkdv - kQueueDq && kQueueDkdv + kXCD * kQueueStride <= kHeaderWords,
+                "three equally spaced queue-head blocks inside the header");
+  hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(64), 0, s, header);
   return hipGetLastError();
 }
 

@@ -71,8 +71,8 @@ struct Plan {
   int32_t nkt;            // dK/dV key tiles (kBKB keys each, within one segment)
   int32_t nkpairs;        // dK/dV key-tile pairs per (batch, KV head)
   int32_t nqc;            // compact query rows = ntiles * kBQ
-  int64_t nwg_q;          // workgroups of the query-major kernels
-  int64_t nwg_k;          // workgroups of the key-major kernel
+  int64_t nwg_q;          // work items of the query-major kernels
+  int64_t nwg_k;          // work items of the key-major kernel
   QSeg q[kMaxQSeg];
   KSeg k[kMaxKSeg];
 };
@@ -85,6 +85,44 @@ __host__ __device__ inline int64_t xcd_logical(int64_t w, int64_t n) {
   const int64_t x = w % kXCD, per = n / kXCD, rem = n % kXCD;
   const int64_t base = x * per + (x < rem ? x : rem);
   return base + w / kXCD;
+}
+
+// The kernels take their work items from one queue per XCD: queue x holds
+// the XCD's contiguous block of logical indices above (the order
+// xcd_logical assigns), so the L2 locality of that order is kept, while a
+// workgroup whose own queue is empty takes items from the other queues.
+// The dies do not run at one speed (the same work measured up to 10% apart
+// between the XCDs of one device), so a fixed split of the items leaves
+// the faster dies idle at the end.
+__host__ __device__ inline int64_t queue_base(int64_t n, int x) {
+  const int64_t per = n / kXCD, rem = n % kXCD;
+  return x * per + (x < rem ? x : rem);
+}
+__host__ __device__ inline int64_t queue_len(int64_t n, int x) { return n / kXCD + (x < n % kXCD ? 1 : 0); }
+
+// Workgroups of a launch over `items` work items: one per item, plus a
+// quarter more (rounded up to whole rounds of the eight XCDs).  Workgroups
+// go to the XCDs round-robin, so each die runs the same number; the spares
+// let a die that finishes its own queue early take items from the others,
+// and on the last die to finish they find every queue empty and end.
+inline unsigned queue_grid(int64_t items) {
+  const int64_t spare = (items / 4 + kXCD - 1) / kXCD * kXCD;
+  return (unsigned)(items + spare);
+}
+
+// Next work item of a workgroup on XCD x: its own queue first, then the
+// others in turn; -1 when all are empty.  heads[q * stride] counts the
+// items taken from queue q (zeroed before the launch); *scan counts the
+// queues this workgroup has found empty.  Called by one thread of the
+// workgroup.
+__device__ inline int64_t next_item(int32_t* heads, int stride, int64_t n, int x, int* scan) {
+  while (*scan < kXCD) {
+    const int q = (x + *scan) % kXCD;
+    const int32_t k = atomicAdd(heads + q * stride, 1);
+    if (k < queue_len(n, q)) return queue_base(n, q) + k;
+    ++*scan;
+  }
+  return -1;
 }
 
 // Pair p of the query tiles -> (heavier tile, lighter tile or -1).
@@ -105,8 +143,8 @@ struct WgQ {
 
 // Query-major workgroup w (dispatch order) -> batch, head, its two tiles.
 // Logical order: batch, KV head, pair, query head within the group.
-__host__ __device__ inline WgQ decode_wg_q(const Plan& P, int64_t w) {
-  const int64_t l = xcd_logical(w, P.nwg_q);
+// Logical work item l of the query-major kernels -> (batch, head, tiles).
+__host__ __device__ inline WgQ decode_item_q(const Plan& P, int64_t l) {
   WgQ r;
   const int32_t gq = (int32_t)(l % P.G);
   int64_t rest = l / P.G;
@@ -118,6 +156,8 @@ __host__ __device__ inline WgQ decode_wg_q(const Plan& P, int64_t w) {
   pair_tiles(P, pair, &r.tile_a, &r.tile_b);
   return r;
 }
+// Item w of the exported order: queue w % 8's (w / 8)-th item.
+__host__ __device__ inline WgQ decode_wg_q(const Plan& P, int64_t w) { return decode_item_q(P, xcd_logical(w, P.nwg_q)); }
 
 __host__ __device__ inline int32_t seg_of_tile(const Plan& P, int32_t t) {
   int32_t s = 0;
@@ -240,8 +280,8 @@ struct WgK {
   int32_t b, g, tile_a, tile_b;
 };
 
-__host__ __device__ inline WgK decode_wg_k(const Plan& P, int64_t w) {
-  const int64_t l = xcd_logical(w, P.nwg_k);
+// Logical work item l of the key-major kernel -> (batch, KV head, tiles).
+__host__ __device__ inline WgK decode_item_k(const Plan& P, int64_t l) {
   WgK r;
   const int32_t pair = (int32_t)(l % P.nkpairs);
   const int64_t rest = l / P.nkpairs;
@@ -250,6 +290,8 @@ __host__ __device__ inline WgK decode_wg_k(const Plan& P, int64_t w) {
   kpair_tiles(P, pair, &r.tile_a, &r.tile_b);
   return r;
 }
+// Item w of the exported order: queue w % 8's (w / 8)-th item.
+__host__ __device__ inline WgK decode_wg_k(const Plan& P, int64_t w) { return decode_item_k(P, xcd_logical(w, P.nwg_k)); }
 
 // First row of query segment s that sees any key at or after source row
 // `k0` of a key segment of kind `kkind` (rows are monotone in visibility).

@@ -164,22 +164,28 @@ int bdattn_assign_blocks(int32_t B, int32_t P, int32_t r, int32_t* out);
  * L % (2P) == 0.  Pure host function. */
 int bdattn_clean_shard(int32_t L, int32_t P, int32_t s, bdattn_kv* out);
 
-/* Workgroup work order of the forward kernel for this call (bit-exact
- * contract): for each workgroup in dispatch order, four int32 values
- * (batch, query head, first query tile, second query tile or -1).  Query
+/* Work items of the query-major kernels (forward and dQ) for this call
+ * (bit-exact contract), four int32 values each (batch, query head, first
+ * query tile, second query tile or -1), in queue order: item w is the
+ * (w / 8)-th item of the queue of XCD w % 8, and each XCD's queue holds a
+ * contiguous block of the logical order described next.  A workgroup takes the next item of its own
+ * XCD's queue, or, when that is empty, of the other queues in turn (a
+ * launch has a quarter more workgroups than items, so a die that finishes
+ * early takes over the others' remaining items).  Query
  * tiles are numbered over the share rows in tiles of 128 rows, clean
  * ranges first; within each kind, tile t is paired with its mirror n-1-t so
  * that every workgroup does the same work (dual-end pairing applied to the
  * query tiles of one GPU).  `cap` is the capacity of `items` in int32s;
- * `*n` receives the number of workgroups.  Pure host function. */
+ * `*n` receives the number of work items.  Pure host function. */
 int bdattn_plan_order(const bdattn_problem* problem, const bdattn_share* share,
                       const bdattn_kv* kv, int32_t* items, int64_t cap,
                       int64_t* n);
 
-/* Workgroup work order of the key-major backward kernel (dK/dV) for this
- * call (bit-exact contract), by the same dual-end rule applied to key tiles
+/* Work items of the key-major backward kernel (dK/dV) for this call
+ * (bit-exact contract; queue order and dynamic assignment as for
+ * bdattn_plan_order), by the same dual-end rule applied to key tiles
  * ([P1] "负载均衡：为什么要首尾块配对"; [P3] "Load balancing: pairing early
- * and late blocks"): for each workgroup in dispatch order, four int32 values
+ * and late blocks"): for each work item, four int32 values
  * (batch, KV head, first key tile, second key tile or -1).  Key tiles hold
  * 128 keys of one key segment: the call's clean ranges in order, then its
  * corrupted keys, each segment starting a new tile.  Clean tile t (counted
