@@ -246,8 +246,8 @@ int gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const void* A, int64
             best_ms = ms;
           }
         }
-        hipEventDestroy(e0);
-        hipEventDestroy(e1);
+        (void)hipEventDestroy(e0);  // timing only: a failure here changes no result
+        (void)hipEventDestroy(e1);
       } else {
         for (int i = 0; i < found && pick < 0; ++i)
           if (cand[i].state == HIPBLAS_STATUS_SUCCESS && cand[i].workspaceSize <= kBlasWs) pick = i;
