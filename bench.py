@@ -14,6 +14,7 @@ clean copy.  Printed as one JSON line.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -283,20 +284,28 @@ def report_all(reps=3):
     dev = torch.device("cuda:0")
 
     def timed(fn):
-        """Average ms per call and each kernel's average ms per call."""
+        """Average ms per call and each kernel's average ms per call, over
+        enough calls to fill about 150 ms of GPU time (at least `reps`, at
+        most 50): a few steps of a small workload are too short a window
+        for a stable clock."""
         fn()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        est_ms = (time.perf_counter() - t0) * 1e3
+        n = max(reps, min(50, math.ceil(150.0 / max(est_ms, 1e-3))))
         B.bdattn_profile_read()
         B.bdattn_profile_enable(True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record()
         torch.cuda.synchronize()
         B.bdattn_profile_enable(False)
         prof = B.bdattn_profile_read()
-        return e0.elapsed_time(e1) / reps, {n: t / reps for n, (_, t) in prof.items()}
+        return e0.elapsed_time(e1) / n, {k: t / n for k, (_, t) in prof.items()}
 
     rows = []
     whole = [("fp32_L1K_M16_h4_d64_fwd", 0, (1, 1024, 16, 4, 4, 64), torch.float32, 1.0, False, 0),
