@@ -56,15 +56,18 @@ def sources_sha(paths):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs, scaled by the copy-kernel calibration; None when absent or
-    when the kernel's sources changed since the counters were taken."""
+    WRITE_SIZE runs, scaled by the copy-kernel calibration; None when absent,
+    when the counters were taken on another workload, or when the kernel's
+    sources changed since they were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f).get(kernel)
-    if not rec or not all(os.path.exists(os.path.join(ROOT, r)) for r in rec["sources"]):
+    if not rec or rec.get("workload") != workload:
+        return None
+    if not all(os.path.exists(os.path.join(ROOT, r)) for r in rec["sources"]):
         return None
     if sources_sha(rec["sources"]) != rec["sha256"]:
         return None
@@ -449,13 +452,13 @@ def bench_vocab(args):
     dom_avg = dom_ms / dom_cnt
     ach = dom_flops / (dom_avg * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom_name),
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom_name, args.workload),
             "avg_ms": round(dom_avg, 3), "library": "hipBLASLt"}
     rc, rms = prof["rows"]
     rows_bytes = 6.0 * R * V * args.steps / rc  # fp32 logits read once + bf16 gradient written, per launch
     rach = rows_bytes / (rms / rc * 1e-3) / 1e9
     roof_rows = {"bound": "hbm", "kernel": "rows", "achieved": round(rach, 1), "peak": PEAK_HBM_GBS,
-                 "unit": "GB/s", "frac": round(rach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("vocab_rows"),
+                 "unit": "GB/s", "frac": round(rach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("vocab_rows", args.workload),
                  "avg_ms": round(rms / rc, 3)}
     # the same step with the head trained: dW cleared, then accumulated per chunk
     dw = torch.zeros((V, d), dtype=torch.float32, device=dev)
@@ -708,8 +711,8 @@ def main():
     if dflops is not None:
         ach = dflops / (dom_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom_name),
-                "avg_ms": round(dom_avg, 3)}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom_name, args.workload), "avg_ms": round(dom_avg, 3)}
     cpu = None
     if args.cpu_rows > 0:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)

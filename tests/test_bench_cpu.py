@@ -40,3 +40,15 @@ def test_tile_counts_brute_force(L, M):
 
     vis = sum(seen(qa, ka) for qa in range(0, 2 * L, 128) for ka in range(0, 2 * L, 64))
     assert bench.tile_counts(L, M) == (vis, (2 * L // 128) * (2 * L // 64))
+
+
+def test_traffic_record_only_for_its_workload():
+    """The committed HBM byte counts belong to the workload they were taken
+    on: a bench line of another workload carries none."""
+    import json
+    with open(bench.TRAFFIC_FILE) as f:
+        recs = json.load(f)
+    for kernel, rec in recs.items():
+        assert bench.measured_traffic(kernel, rec["workload"] + "_other") is None
+        got = bench.measured_traffic(kernel, rec["workload"])
+        assert got is None or (isinstance(got, int) and got > 0)
