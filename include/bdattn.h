@@ -65,8 +65,10 @@
  *     bdattn_workspace_bytes).
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL =
  *     the null stream); buffers must stay valid until it completes.  Calls on
- *     one stream are ordered; calls that share output buffers must not run
- *     concurrently on different streams.
+ *     one stream are ordered; calls that share output buffers, or a
+ *     workspace (it holds the call's range flag and the work-queue heads its
+ *     kernels take items from), must not run concurrently on different
+ *     streams.
  *   - Every argument is validated on the host before any HIP call; an invalid
  *     argument returns BDATTN_EINVAL (or ENOTSUP / EWORKSPACE) and enqueues
  *     nothing.  A failed launch returns BDATTN_EHIP.  Nothing aborts or
