@@ -108,9 +108,17 @@ __device__ void dq_tile(const Plan& P, const DqArgs& A, DqSmem<D>& sm, int b, in
       // together, so the wave fits two to a SIMD
       const _Float16* kt = sm.k[buf];
       int32_t vlo = 0, vhi = 0;
-      if (!full) compact_range(P.k[ri], rb, clean, &vlo, &vhi);
+      bool see[2] = {true, true};
+      if (!full) {
+        compact_range(P.k[ri], rb, clean, &vlo, &vhi);
+        see[0] = __any(sees_block32(vlo, vhi, c));
+        see[1] = __any(sees_block32(vlo, vhi, c + 32));
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // a block none of the wave's rows sees (a masked tile's window edge
+        // or another corrupted block's keys) has P = 0: nothing to add
+        if (!see[kb]) continue;
         // S^T = K Q^T and dP^T = V dO^T, as two interleaved chains; the other
         // wave of the SIMD runs its vector work meanwhile
         f32x16 sacc, pacc;

@@ -35,6 +35,26 @@ struct __attribute__((aligned(16))) FwdSmem {
   _Float16 vt[2][TILE];                 // transposed fp16 [d][key], perm16 keys
 };
 
+// One C^T block of 32 rows of a staged natural tile (starting at `block`)
+// times the lane's row held in registers: acc = block row^T, kAhead reads
+// in flight (scores_2kb for a single 32-key block).
+template <int D>
+__device__ __forceinline__ void scores_1kb(const uint16_t* block, int ql, const bf16x8 (&row)[D / 16],
+                                           const LaneOff<D>& o, f32x16& acc) {
+  constexpr int NF = D / 16;
+  const uint16_t* tb = block + ql * D;
+  bf16x8 fr[NF];
+#pragma unroll
+  for (int f = 0; f < kAhead && f < NF; ++f) fr[f] = ld16<bf16x8>(tb + o.nat[f]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + kAhead < NF) fr[f + kAhead] = ld16<bf16x8>(tb + o.nat[f + kAhead]);
+    acc = mfma_bf16(fr[f], row[f], f ? acc : f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Issues the copies of key tile c (compact start) into buffer B.
 template <int D>
 __device__ __forceinline__ void fwd_stage(const FwdArgs& A, const Plan& P, int b, int g, int32_t c, int wave,
@@ -102,6 +122,26 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
         keywalk_at(w, t + 1, &cn, &rn, &fn);
         fwd_stage<D>(A, P, b, g, cn, wave, o, sm, buf ^ 1);
       }
+      // In a masked tile the wave forms scores only for the 32-key blocks
+      // one of its rows sees; the other block's scores are -inf, so its P is
+      // zero and its O products add nothing.  (The window's edges and a
+      // corrupted tile's own-block keys put about an eighth of the products
+      // of the 1,024-token windowed 64K walk in such blocks.  Skipping the
+      // O products too, with a test per product, cost 6% on whole masks.)
+      // The lane's visible range is formed again for the mask rather than
+      // held across the score products, where the registers are all in use.
+      bool see0 = true, see1 = true;
+      if (!full) {
+        int32_t vlo, vhi;
+        compact_range(P.k[ri], rb, clean, &vlo, &vhi);
+        see0 = __any(sees_block32(vlo, vhi, c));
+        see1 = __any(sees_block32(vlo, vhi, c + 32));
+        if (!see0 && !see1) {
+          wait_copies();
+          __syncthreads();
+          return;
+        }
+      }
       // S^T = K Q^T for two blocks of 32 keys.  The two waves sharing a SIMD
       // belong to different workgroups; a wave raises its priority while it
       // issues matrix products and drops it for the softmax, so the other
@@ -109,7 +149,15 @@ __device__ void fwd_tile(const Plan& P, const FwdArgs& A, FwdSmem<D>& sm, int b,
       // competing with it.
       f32x16 sacc[2];
       __builtin_amdgcn_s_setprio(2);
-      scores_2kb<D>(sm.k[buf], ql, qreg, o, sacc);
+      if (see0 && see1) {
+        scores_2kb<D>(sm.k[buf], ql, qreg, o, sacc);
+      } else if (see0) {
+        scores_1kb<D>(sm.k[buf], ql, qreg, o, sacc[0]);
+        sacc[1] = f32x16{} - INFINITY;
+      } else {
+        scores_1kb<D>(sm.k[buf] + 32 * D, ql, qreg, o, sacc[1]);
+        sacc[0] = f32x16{} - INFINITY;
+      }
       __builtin_amdgcn_s_setprio(0);
       // the first V^T fragments of the O products, read under the softmax;
       // fragment f = (s, db), s = 16-key step

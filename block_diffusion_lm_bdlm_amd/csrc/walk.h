@@ -74,4 +74,10 @@ __device__ inline void keywalk_at(const KeyWalk& w, int32_t t, int32_t* c, int32
   *full = *c >= lo && *c + kBK <= hi;
 }
 
+// Whether a row with compact visible range [vlo, vhi) sees any of the 32
+// keys from compact position k0 on.
+__device__ __forceinline__ bool sees_block32(int32_t vlo, int32_t vhi, int32_t k0) {
+  return max(vlo, k0) < min(vhi, k0 + 32);
+}
+
 }  // namespace bd
