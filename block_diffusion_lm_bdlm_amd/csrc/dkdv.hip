@@ -32,6 +32,7 @@
 // position): the last rows are seen by every key tile, so the workgroups
 // resident on one XCD stay on the same rows and share them through L2.
 #include <climits>
+#include <cstddef>
 #include <type_traits>
 
 #include "device.h"
@@ -74,6 +75,29 @@ struct __attribute__((aligned(16))) DkdvSmem {
   int32_t wn, wper;
 };
 
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
+
+// The lane's per-row values of a step (log2 LSE, D, visible interval; rows
+// hh * 4 + 8 i4 + 32 rb + 0..3) are read at one base address plus constant
+// offsets.  The base is formed in every step behind an empty asm: left to
+// itself the compiler forms one address per read, as the arrays lie beyond
+// the 16-bit offset field of the LDS instructions, hoists them out of the
+// walk and spills them, and every reload then stalls its read.
+template <int D>
+__device__ __forceinline__ uint32_t row_vals_base(const DkdvSmem<D>& sm, int hh) {
+  uint32_t a = (uint32_t)(uintptr_t)(lds_void*)&sm.lse2[0][hh * 4];
+  asm volatile("" : "+v"(a));
+  return a;
+}
+// Byte offset of row r of buffer B of a per-row array (its offset in the
+// shared block given) from that base.
+template <int D>
+__device__ __forceinline__ constexpr uint32_t row_vals_off(size_t array_off, int B, int r) {
+  return (uint32_t)(array_off - offsetof(DkdvSmem<D>, lse2)) + (uint32_t)(B * kBQB + r) * 4u;
+}
+
 // Issues the copies of one step (64 rows from compact row cq of head hb)
 // into buffer B: copying wave cw (of kCopyWaves, lane offsets oc) copies
 // its share of each tile.
@@ -113,6 +137,7 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
   constexpr int NF = kRB * NKS;
   f16x8 fr[NF];
   f32x4 l4s[kRB][4];  // log2 LSE of this lane's rows, read while the last products run
+  const uint32_t rv = row_vals_base<D>(sm, hh);
 #pragma unroll
   for (int f = 0; f < kAhead; ++f) fr[f] = ld16<f16x8>(qb + (f / NKS) * 32 * D + o.nat[f % NKS]);
   __builtin_amdgcn_sched_barrier(0);
@@ -126,7 +151,8 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) l4s[rb][i4] = *reinterpret_cast<const f32x4*>(&sm.lse2[B][rb * 32 + i4 * 8 + hh * 4]);
+        for (int i4 = 0; i4 < 4; ++i4)
+          l4s[rb][i4] = *(lds_f32x4*)(rv + row_vals_off<D>(offsetof(DkdvSmem<D>, lse2), B, rb * 32 + i4 * 8));
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -137,14 +163,12 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
   for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int r = rb * 32 + i4 * 8 + hh * 4;
+      const int r = rb * 32 + i4 * 8;
       const f32x4 l4 = l4s[rb][i4];
-      int32_t los[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, his[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+      i32x4 los = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, his = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
       if constexpr (!FULL) {
-        const int4 lo4 = *reinterpret_cast<const int4*>(&sm.vlo[B][r]);
-        const int4 hi4 = *reinterpret_cast<const int4*>(&sm.vhi[B][r]);
-        los[0] = lo4.x; los[1] = lo4.y; los[2] = lo4.z; los[3] = lo4.w;
-        his[0] = hi4.x; his[1] = hi4.y; his[2] = hi4.z; his[3] = hi4.w;
+        los = *(lds_i32x4*)(rv + row_vals_off<D>(offsetof(DkdvSmem<D>, vlo), B, r));
+        his = *(lds_i32x4*)(rv + row_vals_off<D>(offsetof(DkdvSmem<D>, vhi), B, r));
       }
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
@@ -152,7 +176,8 @@ __device__ __forceinline__ void s_phase_a(DkdvSmem<D>& sm, int B, int kw, int la
         for (int e = 0; e < 4; ++e) {
           const int i = i4 * 4 + e;
           float x = fmaf(sacc[rb][kb][i], c2, -l4[e]);
-          if constexpr (!FULL) x = (mysrc[kb] >= los[e] && mysrc[kb] < his[e]) ? x : -INFINITY;
+          // both bounds tested (no short circuit, which the compiler turns into a branch per value)
+          if constexpr (!FULL) x = ((mysrc[kb] >= los[e]) & (mysrc[kb] < his[e])) ? x : -INFINITY;
           pf[rb][kb][i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(x);
         }
     }
@@ -209,6 +234,7 @@ template <int D>
 __device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, int hh, const f16x8 (&vreg)[kKB][D / 16],
                                           const LaneOff<D>& o, f32x16 (&pacc)[kRB][kKB], f32x4 (&dcs)[kRB][4]) {
   const _Float16* ob = &sm.dO[B][ql * D];
+  const uint32_t rv = row_vals_base<D>(sm, hh);
   constexpr int NKS = D / 16, NF = kRB * NKS;
   f16x8 fr[NF];
 #pragma unroll
@@ -224,7 +250,8 @@ __device__ __forceinline__ void p_phase_a(DkdvSmem<D>& sm, int B, int ql, int hh
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) dcs[rb][i4] = *reinterpret_cast<const f32x4*>(&sm.dc[B][rb * 32 + i4 * 8 + hh * 4]);
+        for (int i4 = 0; i4 < 4; ++i4)
+          dcs[rb][i4] = *(lds_f32x4*)(rv + row_vals_off<D>(offsetof(DkdvSmem<D>, dc), B, rb * 32 + i4 * 8));
     }
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -472,11 +499,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(const Plan P, const DkdvArgs A) {
   __shared__ DkdvSmem<D> sm;
   __shared__ int64_t item;
-  // one work item from the XCD queues (plan.h); a spare workgroup that
-  // finds every queue empty ends here
+  // one work item from the XCD queues, longest first (plan.h); a spare
+  // workgroup that finds every queue empty ends here
   if (threadIdx.x == 0) {
     int scan = 0;
-    item = next_item(A.queue, kQueueStride, P.nwg_k, (int)(blockIdx.x % kXCD), &scan);
+    item = next_item_k(P, A.queue, kQueueStride, (int)(blockIdx.x % kXCD), &scan);
   }
   __syncthreads();
   const int64_t l = item;

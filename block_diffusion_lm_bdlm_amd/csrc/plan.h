@@ -280,6 +280,40 @@ struct WgK {
   int32_t b, g, tile_a, tile_b;
 };
 
+// The key-major kernel's queues hand out their blocks longest first: the
+// k-th claim on queue q takes the block's clean pairs (long walks) in
+// order, then its local tiles (a few steps each).  In the logical order the
+// local tiles sit between rounds of long items; at 8K (two long items per
+// CU) a workgroup of the second round then at times waited a whole item
+// for a CU of one shader engine while a CU of another engine stood idle,
+// and the launch took 2.6 instead of 1.9 ms.  Items are l = group * np + p,
+// pair p < pc a clean pair; nlong(m) counts the clean pairs below item m.
+__host__ __device__ inline int64_t ktile_claim(const Plan& P, int q, int64_t k) {
+  const int64_t n = P.nwg_k, np = P.nkpairs, pc = (n_clean_ktiles(P) + 1) / 2, ns = np - pc;
+  const int64_t b0 = queue_base(n, q), b1 = b0 + queue_len(n, q);
+  auto nlong = [&](int64_t m) { return (m / np) * pc + (m % np < pc ? m % np : pc); };
+  const int64_t l0 = nlong(b0), nl = nlong(b1) - l0;
+  if (k < nl) {
+    const int64_t j = l0 + k;
+    return (j / pc) * np + j % pc;
+  }
+  if (ns == 0) return -1;  // not reached: a block without local tiles has only long items
+  const int64_t j = (b0 - l0) + (k - nl);  // short items below b0, plus the rank in the block
+  return (j / ns) * np + pc + j % ns;
+}
+
+// next_item for the key-major kernel, in ktile_claim order.
+__device__ inline int64_t next_item_k(const Plan& P, int32_t* heads, int stride, int x, int* scan) {
+  const int64_t n = P.nwg_k;
+  while (*scan < kXCD) {
+    const int q = (x + *scan) % kXCD;
+    const int32_t k = atomicAdd(heads + q * stride, 1);
+    if (k < queue_len(n, q)) return ktile_claim(P, q, k);
+    ++*scan;
+  }
+  return -1;
+}
+
 // Logical work item l of the key-major kernel -> (batch, KV head, tiles).
 __host__ __device__ inline WgK decode_item_k(const Plan& P, int64_t l) {
   WgK r;
@@ -290,8 +324,10 @@ __host__ __device__ inline WgK decode_item_k(const Plan& P, int64_t l) {
   kpair_tiles(P, pair, &r.tile_a, &r.tile_b);
   return r;
 }
-// Item w of the exported order: queue w % 8's (w / 8)-th item.
-__host__ __device__ inline WgK decode_wg_k(const Plan& P, int64_t w) { return decode_item_k(P, xcd_logical(w, P.nwg_k)); }
+// Item w of the exported order: the (w / 8)-th item queue w % 8 hands out.
+__host__ __device__ inline WgK decode_wg_k(const Plan& P, int64_t w) {
+  return decode_item_k(P, ktile_claim(P, (int)(w % kXCD), w / kXCD));
+}
 
 // First row of query segment s that sees any key at or after source row
 // `k0` of a key segment of kind `kkind` (rows are monotone in visibility).

@@ -184,8 +184,11 @@ int bdattn_plan_order(const bdattn_problem* problem, const bdattn_share* share,
                       int64_t* n);
 
 /* Work items of the key-major backward kernel (dK/dV) for this call
- * (bit-exact contract; queue order and dynamic assignment as for
- * bdattn_plan_order), by the same dual-end rule applied to key tiles
+ * (bit-exact contract; queues and dynamic assignment as for
+ * bdattn_plan_order, except that each queue hands out its block longest
+ * first: item w is the (w / 8)-th item queue w % 8 hands out, its block's
+ * clean-tile pairs in logical order, then its corrupted-key tiles), by the
+ * same dual-end rule applied to key tiles
  * ([P1] "负载均衡：为什么要首尾块配对"; [P3] "Load balancing: pairing early
  * and late blocks"): for each work item, four int32 values
  * (batch, KV head, first key tile, second key tile or -1).  Key tiles hold

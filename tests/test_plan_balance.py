@@ -29,13 +29,23 @@ def _xcd_order(logical):
 
 def _key_order_reference(batch, hkv, clean_tiles, local_tiles):
     """Logical index = (b*hkv + g)*npairs + pair; clean pair p holds tiles
-    (p, nc-1-p), -1 when they coincide; local tiles follow singly; XCD x =
-    w % 8 runs a contiguous block of logical indices."""
+    (p, nc-1-p), -1 when they coincide; local tiles follow singly.  XCD x =
+    w % 8 runs a contiguous block of logical indices and hands it out
+    longest first: the block's clean pairs in order, then its local tiles."""
     nc = clean_tiles
     pairs = [(p, -1 if p == nc - 1 - p else nc - 1 - p) for p in range((nc + 1) // 2)]
     pairs += [(nc + t, -1) for t in range(local_tiles)]
     logical = [(b, g, a, c) for b in range(batch) for g in range(hkv) for a, c in pairs]
-    return _xcd_order(logical)
+    N = len(logical)
+    per, rem = divmod(N, 8)
+    sizes = [per + (1 if x < rem else 0) for x in range(8)]
+    starts = np.cumsum([0] + sizes[:-1])
+    queues = []
+    for x in range(8):
+        block = logical[starts[x]:starts[x] + sizes[x]]
+        longs = [it for it in block if it[2] < nc]
+        queues.append(longs + [it for it in block if it[2] >= nc])
+    return np.array([queues[w % 8][w // 8] for w in range(N)], dtype=np.int32)
 
 
 def _calls(name):
