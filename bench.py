@@ -28,10 +28,16 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {
-    # name: (batch, L, M, hq, hkv, d)
+    # name: (batch, L, M, hq, hkv, d[, clean-key window in tokens])
     "bdlm_L64K_M32_h40kv8_d128": (1, 65536, 32, 40, 8, 128),
     "bdlm_L8K_M32_b2_h16kv8_d128": (2, 8192, 32, 16, 8, 128),
+    "bdlm_L64K_M32_h40kv8_d128_window1024": (1, 65536, 32, 40, 8, 128, 1024),
 }
+
+
+def whole_workload(work):
+    """(batch, L, M, hq, hkv, d, window) of a WORKLOADS entry (window 0: none)."""
+    return tuple(work[:6]) + ((work[6] if len(work) > 6 else 0),)
 DEFAULT = "bdlm_L64K_M32_h40kv8_d128"
 # One GPU's CSBP share: name -> (seed index, L, M, hq, hkv, P, clean-shard
 # query rows, outlier fraction); rank 0, d = 128.
@@ -106,21 +112,25 @@ def visible_pairs(L, M, window=0, token_causal=False):
     return int(clean.sum() + corr.sum())
 
 
-def tile_counts(L, M, qt=128, kt=64):
+def tile_counts(L, M, qt=128, kt=64, window=0):
     """(visited, total) (query tile, key tile) pairs per head of the whole
     block-causal mask at the forward kernel's granularity (128 query rows,
     64 keys), from the mask geometry: a clean query tile sees the clean
     keys up to the end of its last row's block; a corrupted query tile sees
     the clean keys before its last row's block and the corrupted keys of
-    its own blocks.  Key tiles of the clean and corrupted key spaces start
-    at 0 and at L."""
+    its own blocks.  With a clean-key window W, the tile's first row sees
+    clean keys from its position - W + 1 on (exact for W > M, where the
+    rows of a tile together see one unbroken key range).  Key tiles of the
+    clean and corrupted key spaces start at 0 and at L."""
     a = np.arange(0, L, qt, dtype=np.int64)
     last = np.minimum(a + qt, L) - 1
+    lo = np.maximum(0, a - window + 1) // kt * kt if window > 0 else np.zeros_like(a)
     clean_end = (last // M + 1) * M
-    visited = ((clean_end + kt - 1) // kt).sum()
+    visited = ((clean_end + kt - 1) // kt - lo // kt).sum()
     corr_clean = (last // M) * M
     own_lo, own_hi = (a // M) * M, (last // M + 1) * M
-    visited += ((corr_clean + kt - 1) // kt).sum() + ((own_hi + kt - 1) // kt - own_lo // kt).sum()
+    visited += np.where(corr_clean > lo, (corr_clean + kt - 1) // kt - lo // kt, 0).sum()
+    visited += ((own_hi + kt - 1) // kt - own_lo // kt).sum()
     nkt = 2 * ((L + kt - 1) // kt)
     return int(visited), int(2 * len(a) * nkt)
 
@@ -182,7 +192,7 @@ def cpu_baseline(work, q, k, v, do, nrows, seed=0):
     import torch
 
     from oracle import oracle as orc
-    batch, L, M, hq, hkv, d = work
+    batch, L, M, hq, hkv, d, window = whole_workload(work)
     G = hq // hkv
     rng = np.random.default_rng(seed)
     pos = rng.integers(0, 2 * L, size=nrows)
@@ -198,14 +208,17 @@ def cpu_baseline(work, q, k, v, do, nrows, seed=0):
     idx = torch.as_tensor(pos, device=q.device)
     hq_[0, pos, :G] = host_full(q[0, idx, :G])
     hdo[0, pos, :G] = host_full(do[0, idx, :G])
-    p = orc.problem(batch, L, M, hq, hkv, d, bf16=True)
+    p = orc.problem(batch, L, M, hq, hkv, d, bf16=True, window=window)
     t0 = time.perf_counter()
     orc.dq_rows(p, orc.keys(), orc.keys(), hq_, hk, hv, hdo, bsel, heads, pos)
     dt = time.perf_counter() - t0
-    # visible keys of each sampled row (block-causal clean copy)
+    # visible keys of each sampled row (block-causal clean copy; clean keys
+    # from t - W + 1 on under a window W; a corrupted row adds its own block)
     t = np.where(pos < L, pos, pos - L)
     blk = t // M
-    nvis = np.where(pos < L, (blk + 1) * M, (blk + 1) * M)
+    lo = np.maximum(0, t - window + 1) if window > 0 else np.zeros_like(t)
+    clean_hi = np.where(pos < L, (blk + 1) * M, blk * M)
+    nvis = np.maximum(0, clean_hi - lo) + np.where(pos < L, 0, M)
     flops = float(nvis.sum()) * 8 * d  # forward 4d + dQ part of the backward 4d
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
             "sample": f"fp64 forward + dQ of {nrows} seeded (row, head) pairs of KV group 0; "
@@ -641,7 +654,7 @@ def main():
 
     dev = torch.device("cuda:0")
     work = WORKLOADS[args.workload]
-    batch, L, M, hq, hkv, d = work
+    batch, L, M, hq, hkv, d, window = whole_workload(work)
     seed = synth.SEED_BASE + 2
     n2 = 2 * L
     print(f"[bench] generating inputs for {args.workload}", file=sys.stderr, flush=True)
@@ -649,7 +662,7 @@ def main():
     k = synth.normal((batch, n2, hkv, d), seed, "k", dev)
     v = synth.normal((batch, n2, hkv, d), seed, "v", dev)
     do = synth.normal((batch, n2, hq, d), seed, "do", dev)
-    wm = WholeMask(batch, L, M, hq, hkv, d)
+    wm = WholeMask(batch, L, M, hq, hkv, d, window=window)
     ws_f = wm.workspace(False, dev)
     ws_b = wm.workspace(True, dev)
     grads = wm.alloc_grads(dev)
@@ -703,8 +716,8 @@ def main():
           + ", ".join(f"{n} {c}x {t / c:.3f} ms" for n, (c, t) in sorted(prof.items(), key=lambda x: -x[1][1])),
           file=sys.stderr, flush=True)
 
-    pairs = visible_pairs(L, M)
-    tiles = tile_counts(L, M)
+    pairs = visible_pairs(L, M, window)
+    tiles = tile_counts(L, M, window=window)
     useful = 14.0 * d * pairs * hq * batch
     tflops = useful / (ms * 1e-3) / 1e12
     # dominant kernel by time
@@ -724,7 +737,8 @@ def main():
         cpu = cpu_baseline(work, q, k, v, do, args.cpu_rows)
     kernels = {n: {"launches": c, "avg_ms": round(t / c, 4)} for n, (c, t) in prof.items()}
     out = {
-        "metric": "useful attention TFLOP/s fwd+bwd at 64K (1 GPU); % of bf16 MFMA peak",
+        "metric": ("useful attention TFLOP/s fwd+bwd at 64K (1 GPU); % of bf16 MFMA peak" if args.workload == DEFAULT
+                   else f"useful attention TFLOP/s fwd+bwd, {args.workload} (1 GPU); % of bf16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -737,7 +751,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic N(0,1) bf16 inputs, seeded",
         "config": {"workload": args.workload, "batch": batch, "L": L, "positions": n2, "M": M, "hq": hq,
-                   "hkv": hkv, "d": d, "clean_mask": "block-causal", "parallelism": "single GPU"},
+                   "hkv": hkv, "d": d, "clean_mask": "block-causal", "window": window, "parallelism": "single GPU"},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(batch * L / (ms * 1e-3), 1),
         "positions_per_s": round(batch * n2 / (ms * 1e-3), 1),

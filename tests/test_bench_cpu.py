@@ -42,6 +42,42 @@ def test_tile_counts_brute_force(L, M):
     assert bench.tile_counts(L, M) == (vis, (2 * L // 128) * (2 * L // 64))
 
 
+@pytest.mark.parametrize("L,M,W", [(256, 32, 100), (384, 16, 130), (512, 32, 64), (256, 32, 33), (384, 16, 17)])
+def test_tile_counts_window_brute_force(orc, L, M, W):
+    """Visited tile pairs under a clean-key window of at least M + 1 tokens,
+    against a pair-by-pair scan of the oracle's mask predicate."""
+    p = orc.problem(1, L, M, 1, 1, 4, window=W)
+
+    def seen(qa, ka):
+        return any(orc.visible(p, r, k) for r in range(qa, min(qa + 128, 2 * L))
+                   for k in range(ka, min(ka + 64, 2 * L)))
+
+    vis = sum(seen(qa, ka) for qa in range(0, 2 * L, 128) for ka in range(0, 2 * L, 64))
+    assert bench.tile_counts(L, M, window=W) == (vis, (2 * L // 128) * (2 * L // 64))
+
+
+def test_cpu_baseline_row_counts_match_oracle_mask(orc):
+    """The CPU baseline prices each sampled row by its visible keys: the same
+    count as the oracle's predicate, with and without a window."""
+    L, M = 96, 8
+    for W in (0, 20):
+        p = orc.problem(1, L, M, 1, 1, 4, window=W)
+        pos = np.arange(2 * L)
+        t = np.where(pos < L, pos, pos - L)
+        blk = t // M
+        lo = np.maximum(0, t - W + 1) if W > 0 else np.zeros_like(t)
+        clean_hi = np.where(pos < L, (blk + 1) * M, blk * M)
+        nvis = np.maximum(0, clean_hi - lo) + np.where(pos < L, 0, M)
+        ref = [sum(orc.visible(p, i, j) for j in range(2 * L)) for i in range(2 * L)]
+        assert list(nvis) == ref
+
+
+def test_whole_workload_window_field():
+    for name, work in bench.WORKLOADS.items():
+        w = bench.whole_workload(work)
+        assert len(w) == 7 and w[6] == (1024 if name.endswith("window1024") else 0)
+
+
 def test_traffic_record_only_for_its_workload():
     """The committed HBM byte counts belong to the workload they were taken
     on: a bench line of another workload carries none."""
